@@ -1,0 +1,257 @@
+"""Pins for the fp64 oracle against facts outside itself.
+
+The pages print no worked example, so each check below is a closed form, an
+invariant of softmax attention, a high-precision brute force on tiny inputs,
+or an independent library (torch's CPU attention in fp64).  Together they
+are chosen so that a dropped term, a wrong sign, a wrong index, a transposed
+operand, a missing scale, a base-2 log or an overflow in the oracle fails at
+least one of them.
+"""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, rtol=1e-12, atol=1e-12):
+    np.testing.assert_allclose(a, b, rtol=rtol, atol=atol)
+
+
+def _brute_mp(q, k, v, scale):
+    """Pure-Python, 50-digit evaluation of the definition, for tiny shapes only."""
+    mpmath.mp.dps = 50
+    B, H, S, D = q.shape
+    Skv = k.shape[2]
+    o = np.zeros((B, H, S, D))
+    lse = np.zeros((B, H, S))
+    for b in range(B):
+        for h in range(H):
+            for i in range(S):
+                s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(float(q[b, h, i, d])) * mpmath.mpf(float(k[b, h, j, d]))
+                                                     for d in range(D)) for j in range(Skv)]
+                w = [mpmath.exp(x) for x in s]
+                tot = mpmath.fsum(w)
+                lse[b, h, i] = float(mpmath.log(tot))
+                for d in range(D):
+                    o[b, h, i, d] = float(mpmath.fsum(w[j] * mpmath.mpf(float(v[b, h, j, d])) for j in range(Skv)) / tot)
+    return o, lse
+
+
+@pytest.mark.parametrize("S,Skv,D", [(1, 1, 1), (3, 5, 2), (8, 8, 4), (5, 7, 3)])
+def test_brute_force_high_precision(S, Skv, D):
+    r = _rng(S * 100 + Skv * 10 + D)
+    q, k, v = r.standard_normal((1, 2, S, D)) * 2, r.standard_normal((1, 2, Skv, D)) * 2, r.standard_normal((1, 2, Skv, D))
+    scale = 1 / math.sqrt(D)
+    o, lse = oracle.attention(q, k, v, scale)
+    o2, lse2 = _brute_mp(q, k, v, scale)
+    _close(o, o2, rtol=1e-13, atol=1e-14)
+    _close(lse, lse2, rtol=1e-13, atol=1e-14)
+
+
+def test_single_key_returns_its_value_row():
+    r = _rng(1)
+    q, k, v = r.standard_normal((2, 3, 9, 16)), r.standard_normal((2, 3, 1, 16)), r.standard_normal((2, 3, 1, 16))
+    o, lse = oracle.attention(q, k, v, 0.25)
+    _close(o, np.broadcast_to(v, o.shape), rtol=0, atol=0)
+    _close(lse, 0.25 * np.einsum("bhid,bhjd->bhi", q, k), rtol=1e-14)
+
+
+def test_two_keys_closed_form():
+    r = _rng(2)
+    q, k, v = r.standard_normal((1, 2, 6, 8)) * 3, r.standard_normal((1, 2, 2, 8)), r.standard_normal((1, 2, 2, 8))
+    sc = 0.3
+    s = sc * np.einsum("bhid,bhjd->bhij", q, k)
+    s0, s1 = s[..., 0], s[..., 1]
+    lse_want = np.logaddexp(s0, s1)
+    sig = lambda x: 1.0 / (1.0 + np.exp(-x))
+    o_want = sig(s0 - s1)[..., None] * v[:, :, None, 0, :] + sig(s1 - s0)[..., None] * v[:, :, None, 1, :]
+    o, lse = oracle.attention(q, k, v, sc)
+    _close(o, o_want)
+    _close(lse, lse_want)
+
+
+def test_zero_queries_give_uniform_weights():
+    r = _rng(3)
+    Skv = 37
+    q = np.zeros((1, 2, 4, 8))
+    k, v = r.standard_normal((1, 2, Skv, 8)), r.standard_normal((1, 2, Skv, 8))
+    o, lse, p = oracle.attention(q, k, v, 0.7, want_p=True)
+    _close(p, np.full(p.shape, 1.0 / Skv), rtol=1e-14, atol=0)
+    _close(lse, np.full(lse.shape, math.log(Skv)), rtol=1e-15, atol=0)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape))
+
+
+def test_softmax_rows_sum_to_one():
+    r = _rng(4)
+    q, k, v = r.standard_normal((1, 3, 20, 32)) * 2, r.standard_normal((1, 3, 300, 32)) * 2, r.standard_normal((1, 3, 300, 32))
+    _, _, p = oracle.attention(q, k, v, 1 / math.sqrt(32), want_p=True)
+    assert np.all(p >= 0)
+    _close(p.sum(-1), np.ones(p.shape[:-1]), rtol=0, atol=1e-13)
+
+
+def test_uniform_values_return_that_value():
+    r = _rng(5)
+    q, k = r.standard_normal((1, 2, 10, 16)) * 3, r.standard_normal((1, 2, 50, 16)) * 3
+    row = r.standard_normal(16)
+    v = np.broadcast_to(row, (1, 2, 50, 16)).copy()
+    o, _ = oracle.attention(q, k, v, 0.25)
+    _close(o, np.broadcast_to(row, o.shape), rtol=1e-13, atol=1e-14)
+
+
+def test_one_hot_dominant_selects_single_value_row():
+    # K_j = c e_j, Q_i = c e_pi(i): s_ij = c^2 scale delta(j, pi(i)).
+    D = Skv = 16
+    S = 16
+    scale = 1 / math.sqrt(D)
+    c = math.sqrt(50.0 / scale)
+    perm = _rng(6).permutation(Skv)
+    k = np.zeros((1, 1, Skv, D))
+    q = np.zeros((1, 1, S, D))
+    for j in range(Skv):
+        k[0, 0, j, j] = c
+    for i in range(S):
+        q[0, 0, i, perm[i]] = c
+    v = _rng(7).standard_normal((1, 1, Skv, D))
+    o, lse = oracle.attention(q, k, v, scale)
+    a = c * c * scale
+    _close(o[0, 0], v[0, 0, perm], rtol=1e-15, atol=1e-15)
+    _close(lse[0, 0], np.full(S, a + math.log1p((Skv - 1) * math.exp(-a))), rtol=1e-15, atol=0)
+
+
+def test_planted_match_in_random_sign_keys_large_logits():
+    # Keys are random +-1 vectors; query i is c times key pi(i).  The planted key beats any
+    # other by at least 2*c*scale per differing sign, so it takes all the weight; logits
+    # reach ~1280, which an implementation without the max shift would overflow on.
+    r = _rng(8)
+    D, Skv, S = 64, 300, 40
+    scale = 1 / math.sqrt(D)
+    k = r.choice([-1.0, 1.0], size=(1, 1, Skv, D))
+    gram = k[0, 0] @ k[0, 0].T
+    np.fill_diagonal(gram, -D)
+    assert gram.max() <= D - 2
+    c = 20.0 / scale
+    pi = r.choice(Skv, size=S, replace=False)
+    q = c * k[:, :, pi, :]
+    v = r.standard_normal((1, 1, Skv, D))
+    o, lse = oracle.attention(q, k, v, scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    _close(o[0, 0], v[0, 0, pi], rtol=0, atol=1e-12)
+    _close(lse[0, 0], np.full(S, c * scale * D), rtol=1e-15, atol=0)
+
+
+def test_affine_map_of_values_commutes():
+    r = _rng(9)
+    q, k, v = r.standard_normal((1, 2, 12, 16)), r.standard_normal((1, 2, 40, 16)), r.standard_normal((1, 2, 40, 16))
+    o, lse = oracle.attention(q, k, v, 0.25)
+    o2, lse2 = oracle.attention(q, k, -2.5 * v + 0.75, 0.25)
+    _close(o2, -2.5 * o + 0.75)
+    _close(lse2, lse, rtol=0, atol=0)
+
+
+def test_joint_key_value_permutation_invariance():
+    r = _rng(10)
+    q, k, v = r.standard_normal((1, 2, 12, 16)), r.standard_normal((1, 2, 40, 16)), r.standard_normal((1, 2, 40, 16))
+    perm = r.permutation(40)
+    o, lse = oracle.attention(q, k, v, 0.25)
+    o2, lse2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.25)
+    _close(o2, o)
+    _close(lse2, lse)
+    # permuting the values alone must change the output
+    o3, _ = oracle.attention(q, k, v[:, :, perm], 0.25)
+    assert np.max(np.abs(o3 - o)) > 1e-3
+
+
+def test_key_shift_moves_lse_only():
+    r = _rng(11)
+    q, k, v = r.standard_normal((1, 2, 12, 16)), r.standard_normal((1, 2, 40, 16)), r.standard_normal((1, 2, 40, 16))
+    u = r.standard_normal(16)
+    o, lse = oracle.attention(q, k, v, 0.25)
+    o2, lse2 = oracle.attention(q, k + u, v, 0.25)
+    _close(o2, o, rtol=1e-11, atol=1e-12)
+    _close(lse2, lse + 0.25 * np.einsum("bhid,d->bhi", q, u), rtol=1e-12, atol=1e-12)
+
+
+def test_torch_cpu_attention_agrees():
+    torch = pytest.importorskip("torch")
+    r = _rng(12)
+    q, k, v = r.standard_normal((2, 3, 33, 64)), r.standard_normal((2, 3, 70, 64)), r.standard_normal((2, 3, 70, 64))
+    scale = 1 / 8.0
+    o, lse = oracle.attention(q, k, v, scale)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ot = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale).numpy()
+    lt = torch.logsumexp(scale * torch.matmul(tq, tk.transpose(-1, -2).contiguous()), dim=-1).numpy()
+    _close(o, ot, rtol=1e-11, atol=1e-12)
+    _close(lse, lt, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("lens,order", [
+    ((64, 64, 64, 64), (0, 1, 2, 3)),
+    ((30, 0, 97, 1, 128), (4, 2, 0, 3, 1)),
+    ((100, 156), (1, 0)),
+    ((256,), (0,)),
+])
+def test_chunk_partials_merge_to_unchunked(lens, order):
+    r = _rng(13)
+    q, k, v = r.standard_normal((1, 2, 24, 32)) * 2, r.standard_normal((1, 2, 256, 32)) * 2, r.standard_normal((1, 2, 256, 32))
+    o, lse = oracle.attention(q, k, v, 0.2)
+    parts = oracle.chunk_partials(q, k, v, 0.2, lens)
+    om, lm = oracle.lse_merge([parts[c][0] for c in order], [parts[c][1] for c in order])
+    _close(om, o)
+    _close(lm, lse)
+    # ring-style online merge, two at a time, in the same order
+    acc_o, acc_l = parts[order[0]]
+    for c in order[1:]:
+        acc_o, acc_l = oracle.lse_merge([acc_o, parts[c][0]], [acc_l, parts[c][1]])
+    _close(acc_o, o)
+    _close(acc_l, lse)
+
+
+def test_empty_key_range_and_merge_edges():
+    r = _rng(14)
+    q, k, v = r.standard_normal((1, 1, 5, 8)), r.standard_normal((1, 1, 16, 8)), r.standard_normal((1, 1, 16, 8))
+    oe, le = oracle.attention(q, k, v, 0.5, kv_range=(7, 7))
+    assert np.all(oe == 0) and np.all(le == -np.inf)
+    o, lse = oracle.attention(q, k, v, 0.5)
+    # one part: identity; with an empty part: identity; all empty: O = 0, LSE = -inf, no NaN
+    o1, l1 = oracle.lse_merge([o], [lse])
+    _close(o1, o, rtol=0, atol=0)
+    _close(l1, lse, rtol=0, atol=0)
+    o2, l2 = oracle.lse_merge([oe, o, oe], [le, lse, le])
+    _close(o2, o, rtol=1e-15, atol=0)
+    _close(l2, lse, rtol=0, atol=0)
+    o3, l3 = oracle.lse_merge([oe, oe], [le, le])
+    assert np.all(o3 == 0) and np.all(l3 == -np.inf)
+
+
+def test_stored_dtypes_widen_exactly():
+    r = _rng(15)
+    import synth
+    q64 = r.standard_normal((1, 2, 9, 16))
+    k64 = r.standard_normal((1, 2, 30, 16))
+    v64 = r.standard_normal((1, 2, 30, 16))
+    qb, kb, vb = (synth.f32_to_bf16_bits(x.astype(np.float32)) for x in (q64, k64, v64))
+    ob, lb = oracle.attention(qb, kb, vb, 0.25)
+    qw, kw, vw = (synth.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb))
+    ow, lw = oracle.attention(qw, kw, vw, 0.25)
+    assert np.array_equal(ob, ow) and np.array_equal(lb, lw)
+    of, lf = oracle.attention(q64.astype(np.float32), k64.astype(np.float32), v64.astype(np.float32), 0.25)
+    og, lg = oracle.attention(*(x.astype(np.float32).astype(np.float64) for x in (q64, k64, v64)), 0.25)
+    assert np.array_equal(of, og) and np.array_equal(lf, lg)
+
+
+def test_row_selection_matches_full_rows():
+    r = _rng(16)
+    q, k, v = r.standard_normal((1, 2, 40, 16)), r.standard_normal((1, 2, 33, 16)), r.standard_normal((1, 2, 33, 16))
+    o, lse = oracle.attention(q, k, v, 0.25)
+    rows = [0, 5, 39, 17]
+    os_, ls_ = oracle.attention(q, k, v, 0.25, q_rows=rows)
+    assert np.array_equal(os_, o[:, :, rows]) and np.array_equal(ls_, lse[:, :, rows])
+    oz, lz = oracle.attention(q[:, :, :0], k, v, 0.25)
+    assert oz.shape == (1, 2, 0, 16) and lz.shape == (1, 2, 0)
