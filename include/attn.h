@@ -1,0 +1,167 @@
+/*
+ * attn.h — C ABI of the long-sequence attention library (libattn.so, gfx950).
+ *
+ * The operation is bidirectional (non-causal) multi-head softmax attention,
+ * evaluated blockwise over chunks of the key/value sequence, with the
+ * per-chunk partial results combined by their log-sum-exp.  This is the
+ * per-GPU work of context parallelism in the NVIDIA Technical Blog "Scaling
+ * AI Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+ * Inference Support": section "AllGather KV" (a query slice attends over the
+ * full sequence), section "Ring Attention" (key/value chunks arrive one at a
+ * time and an online softmax folds each into the output, so the full K and V
+ * are never materialised), and section "DeepSpeed Ulysses" (full-sequence
+ * attention on a subset of heads).  Section "Context parallelism" fixes the
+ * attention as bidirectional.
+ *
+ * For query row i of head (b, h) and the keys j of one chunk:
+ *     s_ij = scale * <Q[b,h,i,:], K[b,h,j,:]>,  m_i = max_j s_ij,
+ *     l_i  = sum_j exp(s_ij - m_i),
+ *     O[b,h,i,:] = sum_j exp(s_ij - m_i) / l_i * V[b,h,j,:],
+ *     LSE[b,h,i] = m_i + ln(l_i)               (natural log, scale included).
+ * Two results over disjoint key sets merge exactly:
+ *     LSE = ln(exp(LSE_1) + exp(LSE_2)),
+ *     O   = exp(LSE_1 - LSE) * O_1 + exp(LSE_2 - LSE) * O_2.
+ *
+ * Conventions (shared by every entry point):
+ *  - Tensors are [B, H, S, D] with the d index contiguous (stride 1); the b,
+ *    h and s strides are given in ELEMENTS by attn_strides_t, so [B, S, H, D]
+ *    views work too.  LSE tensors are [B, H, Sq] fp32, contiguous.
+ *  - Every tensor pointer is a DEVICE pointer, 16-byte aligned; every stride
+ *    times the element size must be a multiple of 16 bytes.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the legacy default stream).  Nothing is synchronised by the library.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no state between calls, and is re-entrant.
+ *  - Arguments are checked before anything is launched.  A non-OK status
+ *    means nothing was enqueued and no output was touched, except
+ *    ATTN_ERR_HIP, which reports a failed launch (a later kernel fault shows
+ *    up, as in HIP, at the caller's next synchronisation).  No C++ exception
+ *    crosses this interface.
+ *  - Edge cases: Sq == 0 is a no-op returning ATTN_OK.  A chunk with no keys
+ *    yields O = 0 and LSE = -inf.  Merging parts whose LSE are all -inf
+ *    yields O = 0 and LSE = -inf (no NaN).  Non-finite inputs propagate.
+ *  - Supported: D in {64, 128}; input dtype bf16 (MFMA path, fp32
+ *    accumulation) or fp32 (fp32 throughout); output dtype bf16 or fp32 for
+ *    bf16 inputs, fp32 for fp32 inputs.
+ */
+#ifndef LSDIT_ATTN_H
+#define LSDIT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = 2,       /* negative size, chunk lengths not summing, order not a permutation */
+    ATTN_ERR_DTYPE = 3,       /* unsupported dtype combination */
+    ATTN_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned, or d stride not 1 */
+    ATTN_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128, too many chunks */
+    ATTN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than attn_shard_workspace_size() */
+    ATTN_ERR_HIP = 7          /* a kernel launch failed */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Element strides of the b, h and s indices; the d stride is always 1. */
+typedef struct {
+    int64_t b, h, s;
+} attn_strides_t;
+
+/* An opaque hipStream_t. */
+typedef void* attn_stream_t;
+
+/* Most chunks attn_shard_fwd accepts, and most parts one attn_lse_merge call accepts. */
+#define ATTN_MAX_CHUNKS 64
+
+/* Merge modes of attn_shard_fwd (exactly one). */
+#define ATTN_MERGE_NWAY 1u   /* every chunk writes an fp32 partial; one n-way merge at the end */
+#define ATTN_MERGE_ONLINE 2u /* ring style: after each chunk, a pairwise merge into a running fp32 result */
+#define ATTN_MERGE_FUSED 4u  /* each chunk kernel merges its result into the running fp32 result in its epilogue */
+
+/*
+ * attn_chunk_fwd — attention of every query row against ONE chunk of keys.
+ * (Blog sections "Ring Attention" and "AllGather KV": the per-rank, per-chunk
+ * attention whose output the online softmax later folds together.)
+ *
+ *   q        [B, H, Sq, D] in_dt, strides qs
+ *   k, v     [B, H, Skv, D] in_dt, strides ks, vs (the chunk's rows only)
+ *   scale    softmax scale (1/sqrt(D) for standard attention), finite, > 0
+ *   o        [B, H, Sq, D] o_dt, strides os: the chunk's output, normalised by
+ *            the chunk's own row sum (an fp32 "partial" when o_dt = ATTN_F32)
+ *   lse      [B, H, Sq] fp32 contiguous: the chunk's natural-log LSE
+ * o and lse must not overlap q, k or v.
+ */
+attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t Skv,
+                             int32_t D, float scale, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                             attn_stream_t stream);
+
+/*
+ * attn_lse_merge — merge n results over disjoint key sets, row by row.
+ * (Blog section "Ring Attention": each arriving key/value block updates the
+ * attention output through the online softmax; this is that update, for any
+ * number of blocks at once.)
+ *
+ *   o_parts, lse_parts   HOST arrays of n DEVICE pointers; part c is
+ *                        [B, H, Sq, D] fp32 contiguous and [B, H, Sq] fp32.
+ *   o_out                [B, H, Sq, D] o_dt, strides os
+ *   lse_out              [B, H, Sq] fp32 contiguous
+ * 1 <= n <= ATTN_MAX_CHUNKS.  With o_dt = ATTN_F32 and contiguous strides,
+ * o_out may alias o_parts[0] and lse_out may alias lse_parts[0] (the ring's
+ * in-place online merge); no other overlap is allowed.
+ */
+attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
+                             int32_t H, int32_t Sq, int32_t D, void* o_out, attn_strides_t os, attn_dtype_t o_dt,
+                             float* lse_out, attn_stream_t stream);
+
+/*
+ * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd needs
+ * for this shape, chunk count and merge mode (0 when n_chunks == 1).
+ * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
+ */
+size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
+
+/*
+ * attn_shard_fwd — one GPU's share: its query rows against the whole key
+ * sequence, processed chunk by chunk in the given order, the ring's chunk
+ * loop run locally (blog sections "Ring Attention", "AllGather KV",
+ * "DeepSpeed Ulysses").
+ *
+ *   q          [B, H, Sq, D] in_dt, strides qs
+ *   k, v       [B, H, Skv, D] in_dt, strides ks, vs, Skv = sum of chunk_len
+ *   chunk_len  HOST array of n_chunks lengths >= 0; chunk c covers key rows
+ *              [off_c, off_c + chunk_len[c]) with off_c = sum_{c' < c} chunk_len[c']
+ *   order      HOST permutation of 0..n_chunks-1 giving the processing order,
+ *              or NULL for 0, 1, ..., n_chunks-1
+ *   flags      one of ATTN_MERGE_NWAY, ATTN_MERGE_ONLINE, ATTN_MERGE_FUSED
+ *              (ignored when n_chunks == 1)
+ *   workspace  DEVICE buffer of ws_bytes >= attn_shard_workspace_size(...),
+ *              16-byte aligned (may be NULL when that size is 0)
+ *   o, lse     as in attn_chunk_fwd, for the whole key sequence
+ * 1 <= n_chunks <= ATTN_MAX_CHUNKS.  The result equals attention over all
+ * Skv keys up to rounding, whatever the chunking and order.
+ */
+attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t D,
+                             float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
+                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
+                             attn_dtype_t o_dt, float* lse, attn_stream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_str(attn_status_t s);
+
+/* ATTN_ABI_VERSION of the built library. */
+int32_t attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSDIT_ATTN_H */

@@ -1,0 +1,292 @@
+// C ABI of libattn.so: argument checking, dispatch to the HIP kernels, and
+// the shard driver that runs the key/value chunk loop on one GPU.
+//
+// The chunk loop is the per-rank work of Ring Attention and AllGather-KV
+// context parallelism (NVIDIA Technical Blog "Scaling AI Inference Across
+// Multiple GPUs Using NVIDIA TensorRT with Multi-Device Inference Support",
+// sections "Ring Attention" and "AllGather KV"): each chunk of keys yields a
+// partial output and LSE, and the partials are folded together by their
+// log-sum-exp weights.  Three merge schedules are offered: n-way at the end,
+// ring-style pairwise after every chunk, or fused into each chunk kernel's
+// epilogue.  All of them give attention over the whole key sequence.
+#include "attn.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+using lsdit::FwdArgs;
+using lsdit::MergeArgs;
+using lsdit::Strides;
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t esize(attn_dtype_t d) { return d == ATTN_BF16 ? 2 : 4; }
+inline bool valid_dtype(attn_dtype_t d) { return d == ATTN_F32 || d == ATTN_BF16; }
+inline Strides S(attn_strides_t s) { return Strides{s.b, s.h, s.s}; }
+inline Strides contiguous(int H, int Sq, int D) {
+    return Strides{(int64_t)H * Sq * D, (int64_t)Sq * D, (int64_t)D};
+}
+
+bool strides_ok(attn_strides_t s, size_t es) {
+    if (s.b < 0 || s.h < 0 || s.s < 0) return false;
+    return (s.b * (int64_t)es) % 16 == 0 && (s.h * (int64_t)es) % 16 == 0 && (s.s * (int64_t)es) % 16 == 0;
+}
+
+// Checks shared by attn_chunk_fwd and attn_shard_fwd (Skv < 0 means "not applicable").
+attn_status_t check_common(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                           attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t Skv,
+                           int32_t D, float scale, const void* o, attn_strides_t os, attn_dtype_t o_dt,
+                           const float* lse, bool* noop) {
+    *noop = false;
+    if (!valid_dtype(in_dt) || !valid_dtype(o_dt)) return ATTN_ERR_DTYPE;
+    if (in_dt == ATTN_F32 && o_dt != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || Sq < 0) return ATTN_ERR_SHAPE;
+    if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * Sq == 0) {
+        *noop = true;
+        return ATTN_OK;
+    }
+    if (!q || !o || !lse) return ATTN_ERR_NULL;
+    if (Skv != 0 && (!k || !v)) return ATTN_ERR_NULL;
+    const size_t ie = esize(in_dt), oe = esize(o_dt);
+    if (!aligned16(q) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+    if (!strides_ok(qs, ie) || !strides_ok(os, oe)) return ATTN_ERR_ALIGN;
+    if (Skv != 0) {
+        if (!aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
+        if (!strides_ok(ks, ie) || !strides_ok(vs, ie)) return ATTN_ERR_ALIGN;
+    }
+    return ATTN_OK;
+}
+
+hipError_t run_chunk(const FwdArgs& a, attn_dtype_t in_dt, hipStream_t st) {
+    if (a.Skv == 0) {
+        // no keys: O = 0, LSE = -inf, merged with the running result if there is one
+        if (a.prev_o == nullptr) return lsdit::launch_fill_empty(a.o, a.os, a.o_bf16, a.lse, a.B, a.H, a.Sq, a.D, st);
+        MergeArgs m{};
+        m.n = 1;
+        m.o_parts[0] = a.prev_o;
+        m.lse_parts[0] = a.prev_lse;
+        m.B = a.B; m.H = a.H; m.Sq = a.Sq; m.D = a.D;
+        m.o = a.o; m.os = a.os; m.o_bf16 = a.o_bf16; m.lse = a.lse;
+        return lsdit::launch_lse_merge(m, st);
+    }
+    return in_dt == ATTN_BF16 ? lsdit::launch_fwd_bf16(a, st) : lsdit::launch_fwd_f32(a, st);
+}
+
+size_t slot_bytes(int32_t B, int32_t H, int32_t Sq, int32_t D) {
+    const size_t rows = (size_t)B * H * Sq;
+    return align_up(rows * D * 4) + align_up(rows * 4);
+}
+
+int slots_for(uint32_t flags, int32_t n) {
+    if (n <= 1) return 0;
+    if (flags == ATTN_MERGE_NWAY) return n;
+    if (flags == ATTN_MERGE_ONLINE) return 2;
+    if (flags == ATTN_MERGE_FUSED) return 1;
+    return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t Skv,
+                             int32_t D, float scale, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                             attn_stream_t stream) {
+    if (Skv < 0) return ATTN_ERR_SHAPE;
+    bool noop = false;
+    attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, Skv, D, scale, o, os, o_dt, lse, &noop);
+    if (st != ATTN_OK || noop) return st;
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
+    a.o = o; a.os = S(os); a.o_bf16 = o_dt == ATTN_BF16;
+    a.lse = lse;
+    a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
+    a.scale = scale;
+    return run_chunk(a, in_dt, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
+                             int32_t H, int32_t Sq, int32_t D, void* o_out, attn_strides_t os, attn_dtype_t o_dt,
+                             float* lse_out, attn_stream_t stream) {
+    if (!valid_dtype(o_dt)) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (n < 1 || B < 0 || H < 0 || Sq < 0) return ATTN_ERR_SHAPE;
+    if (n > ATTN_MAX_CHUNKS || n > lsdit::kMaxMergeParts) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * Sq == 0) return ATTN_OK;
+    if (!o_parts || !lse_parts || !o_out || !lse_out) return ATTN_ERR_NULL;
+    MergeArgs m{};
+    for (int c = 0; c < n; ++c) {
+        if (!o_parts[c] || !lse_parts[c]) return ATTN_ERR_NULL;
+        if (!aligned16(o_parts[c]) || !aligned16(lse_parts[c])) return ATTN_ERR_ALIGN;
+        m.o_parts[c] = o_parts[c];
+        m.lse_parts[c] = lse_parts[c];
+    }
+    if (!aligned16(o_out) || !aligned16(lse_out) || !strides_ok(os, esize(o_dt))) return ATTN_ERR_ALIGN;
+    m.n = n;
+    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
+    m.o = o_out; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse_out;
+    return lsdit::launch_lse_merge(m, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags) {
+    if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
+    const int slots = slots_for(flags, n_chunks);
+    if (slots <= 0) return 0;
+    return (size_t)slots * slot_bytes(B, H, Sq, D);
+}
+
+attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t D,
+                             float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
+                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
+                             attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
+    // ---- chunk plan (host): lengths, offsets, processing order
+    if (n_chunks < 1) return ATTN_ERR_SHAPE;
+    if (n_chunks > ATTN_MAX_CHUNKS) return ATTN_ERR_UNSUPPORTED;
+    if (!chunk_len) return ATTN_ERR_NULL;
+    int64_t off[ATTN_MAX_CHUNKS];
+    int64_t total = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+        if (chunk_len[c] < 0) return ATTN_ERR_SHAPE;
+        off[c] = total;
+        total += chunk_len[c];
+    }
+    if (total > 0x7FFFFFFF) return ATTN_ERR_SHAPE;
+    int32_t ord[ATTN_MAX_CHUNKS];
+    bool seen[ATTN_MAX_CHUNKS] = {};
+    for (int t = 0; t < n_chunks; ++t) {
+        const int32_t c = order ? order[t] : t;
+        if (c < 0 || c >= n_chunks || seen[c]) return ATTN_ERR_SHAPE;
+        seen[c] = true;
+        ord[t] = c;
+    }
+    if (n_chunks > 1 && slots_for(flags, n_chunks) < 0) return ATTN_ERR_UNSUPPORTED;
+
+    bool noop = false;
+    attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, (int32_t)total, D, scale, o, os, o_dt,
+                                    lse, &noop);
+    if (st != ATTN_OK || noop) return st;
+
+    // chunks without keys carry no weight: drop them from the schedule
+    int32_t live[ATTN_MAX_CHUNKS];
+    int n_live = 0;
+    for (int t = 0; t < n_chunks; ++t)
+        if (chunk_len[ord[t]] > 0) live[n_live++] = ord[t];
+
+    const size_t need = attn_shard_workspace_size(B, H, Sq, D, n_chunks, flags);
+    if (n_live > 1 && need > 0) {
+        if (!workspace || ws_bytes < need) return ATTN_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return ATTN_ERR_ALIGN;
+    }
+
+    const hipStream_t s = (hipStream_t)stream;
+    const size_t ie = esize(in_dt);
+    FwdArgs base{};
+    base.q = q; base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
+    base.B = B; base.H = H; base.Sq = Sq; base.D = D; base.scale = scale;
+    auto chunk_args = [&](int c) {
+        FwdArgs a = base;
+        a.k = (const char*)k + off[c] * ks.s * (int64_t)ie;
+        a.v = (const char*)v + off[c] * vs.s * (int64_t)ie;
+        a.Skv = chunk_len[c];
+        return a;
+    };
+    auto to_final = [&](FwdArgs& a) {
+        a.o = o; a.os = S(os); a.o_bf16 = o_dt == ATTN_BF16; a.lse = lse;
+    };
+    const size_t rows = (size_t)B * H * Sq;
+    const Strides cs = contiguous(H, Sq, D);
+    auto slot_o = [&](int i) { return (float*)((char*)workspace + (size_t)i * slot_bytes(B, H, Sq, D)); };
+    auto slot_lse = [&](int i) { return (float*)((char*)slot_o(i) + align_up(rows * D * 4)); };
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    if (n_live == 0) {
+        return ok(lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s)) ? ATTN_OK
+                                                                                                : ATTN_ERR_HIP;
+    }
+    if (n_live == 1) {
+        FwdArgs a = chunk_args(live[0]);
+        to_final(a);
+        return ok(run_chunk(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
+    }
+
+    if (flags == ATTN_MERGE_FUSED) {
+        for (int t = 0; t < n_live; ++t) {
+            FwdArgs a = chunk_args(live[t]);
+            if (t > 0) {
+                a.prev_o = slot_o(0);
+                a.ps = cs;
+                a.prev_lse = slot_lse(0);
+            }
+            if (t == n_live - 1) {
+                to_final(a);
+            } else {
+                a.o = slot_o(0); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(0);
+            }
+            if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+        }
+        return ATTN_OK;
+    }
+
+    MergeArgs m{};
+    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
+    if (flags == ATTN_MERGE_ONLINE) {
+        for (int t = 0; t < n_live; ++t) {
+            FwdArgs a = chunk_args(live[t]);
+            const int slot = t == 0 ? 0 : 1;
+            a.o = slot_o(slot); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(slot);
+            if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+            if (t == 0) continue;
+            m.n = 2;
+            m.o_parts[0] = slot_o(0); m.lse_parts[0] = slot_lse(0);
+            m.o_parts[1] = slot_o(1); m.lse_parts[1] = slot_lse(1);
+            if (t == n_live - 1) {
+                m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
+            } else {
+                m.o = slot_o(0); m.os = cs; m.o_bf16 = 0; m.lse = slot_lse(0);
+            }
+            if (!ok(lsdit::launch_lse_merge(m, s))) return ATTN_ERR_HIP;
+        }
+        return ATTN_OK;
+    }
+
+    // ATTN_MERGE_NWAY
+    for (int t = 0; t < n_live; ++t) {
+        FwdArgs a = chunk_args(live[t]);
+        a.o = slot_o(t); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(t);
+        if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+        m.o_parts[t] = slot_o(t);
+        m.lse_parts[t] = slot_lse(t);
+    }
+    m.n = n_live;
+    m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
+    return ok(lsdit::launch_lse_merge(m, s)) ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_status_str(attn_status_t s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid shape, scale, chunk lengths or order";
+        case ATTN_ERR_DTYPE: return "unsupported dtype combination";
+        case ATTN_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, chunk count or merge mode";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATTN_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Log-sum-exp merge of per-chunk attention results, and the empty-chunk fill.
+//
+// Results over disjoint key sets combine exactly: with M = max_c LSE_c,
+//   LSE = M + ln sum_c exp(LSE_c - M),   O = sum_c exp(LSE_c - LSE) O_c.
+// This is the online-softmax update that folds each arriving key/value block
+// into a rank's attention output (NVIDIA Technical Blog "Scaling AI
+// Inference Across Multiple GPUs Using NVIDIA TensorRT with Multi-Device
+// Inference Support", section "Ring Attention"), applied to n blocks at once.
+//
+// The merge streams n fp32 partials and writes one output: it is bound by
+// HBM bandwidth.  Each lane owns 4 consecutive elements of a row (16-byte
+// loads), a row's D/4 lanes sit in one wave, and every part is read exactly
+// once.  Parts whose LSE is -inf carry no weight; if all are -inf the output
+// is O = 0, LSE = -inf.
+#include "kernels.h"
+
+#include <math.h>
+
+namespace lsdit {
+namespace {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ void store4(void* o, Strides os, int o_bf16, int H, int Sq, int64_t row, int d, f32x4_t x) {
+    const int64_t bh = row / Sq, s = row % Sq;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t off = b * os.b + h * os.h + s * os.s + d;
+    if (o_bf16) {
+        u32x2_t w;
+        w[0] = pack_bf16(x[0], x[1]);
+        w[1] = pack_bf16(x[2], x[3]);
+        *(u32x2_t*)((unsigned short*)o + off) = w;
+    } else {
+        *(f32x4_t*)((float*)o + off) = x;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+    const int lanes_per_row = a.D / 4;
+    const int rows_per_block = kThreads / lanes_per_row;
+    const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / lanes_per_row;
+    const int d = 4 * (threadIdx.x % lanes_per_row);
+    if (row >= rows) return;
+
+    // natural-log domain, so that a single part with weight exp(0) = 1 passes through exactly
+    float M = -INFINITY;
+    for (int c = 0; c < a.n; ++c) M = fmaxf(M, a.lse_parts[c][row]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float lse_out = -INFINITY;
+    if (M != -INFINITY) {
+        float tot = 0.f;
+        for (int c = 0; c < a.n; ++c) tot += expf(a.lse_parts[c][row] - M);
+        const float L = M + logf(tot);
+        for (int c = 0; c < a.n; ++c) {
+            const float w = expf(a.lse_parts[c][row] - L);
+            const f32x4_t x = *(const f32x4_t*)(a.o_parts[c] + row * a.D + d);
+            acc += w * x;
+        }
+        lse_out = L;
+    }
+    store4(a.o, a.os, a.o_bf16, a.H, a.Sq, row, d, acc);
+    // lse_parts[0] may alias lse: this store depends on every load of it above.
+    if (d == 0) a.lse[row] = lse_out;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_empty_kernel(void* o, Strides os, int o_bf16, float* lse, int H,
+                                                              int Sq, int D, int64_t rows) {
+    const int lanes_per_row = D / 4;
+    const int rows_per_block = kThreads / lanes_per_row;
+    const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / lanes_per_row;
+    const int d = 4 * (threadIdx.x % lanes_per_row);
+    if (row >= rows) return;
+    store4(o, os, o_bf16, H, Sq, row, d, f32x4_t{0.f, 0.f, 0.f, 0.f});
+    if (d == 0) lse[row] = -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
+    const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+    const int rows_per_block = kThreads / (a.D / 4);
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_empty(void* o, Strides os, int o_bf16, float* lse, int B, int H, int Sq, int D,
+                             hipStream_t stream) {
+    const int64_t rows = (int64_t)B * H * Sq;
+    const int rows_per_block = kThreads / (D / 4);
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_empty_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, o, os, o_bf16, lse, H,
+                       Sq, D, rows);
+    return hipGetLastError();
+}
+
+}  // namespace lsdit

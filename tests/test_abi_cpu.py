@@ -1,0 +1,151 @@
+"""The C-ABI library on the host: it loads, exports what include/attn.h declares,
+and rejects bad arguments with the documented status before any HIP call.
+
+No call here reaches a kernel launch: every argument set is invalid, and the
+library checks arguments before touching the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from long_sequence_dit_amd import attn as a
+    if not os.path.exists(a.lib_path()):
+        import long_sequence_dit_amd.build as b
+        b.build()
+    a.load()
+    return a
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src))
+
+
+def test_exports_every_declared_symbol(attn):
+    names = _declared()
+    assert names == set(attn.EXPORTS)
+    lib = ctypes.CDLL(attn.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(attn):
+    lib = attn.load()
+    assert lib.attn_abi_version() == 1
+    for code in range(8):
+        assert len(lib.attn_status_str(code)) > 0
+    assert lib.attn_status_str(99) == b"unknown status"
+
+
+def _st(b, h, s):
+    from long_sequence_dit_amd.attn import Strides
+    return Strides(b, h, s)
+
+
+P = 0x10000  # an aligned, never dereferenced address
+
+
+def _chunk(lib, q=P, k=P, v=P, o=P, lse=P, in_dt=BF16, o_dt=BF16, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1,
+           qs=None, ks=None, vs=None, os_=None):
+    c = _st(2 * 1000 * 128, 1000 * 128, 128)
+    return lib.attn_chunk_fwd(q, qs or c, k, ks or c, v, vs or c, in_dt, B, H, Sq, Skv, D, scale, o, os_ or c, o_dt,
+                              lse, None)
+
+
+def test_chunk_fwd_argument_errors(attn):
+    lib = attn.load()
+    assert _chunk(lib, q=None) == NULL
+    assert _chunk(lib, lse=None) == NULL
+    assert _chunk(lib, k=None) == NULL
+    assert _chunk(lib, in_dt=7) == DTYPE
+    assert _chunk(lib, in_dt=F32, o_dt=BF16) == DTYPE
+    assert _chunk(lib, D=96) == UNSUP
+    assert _chunk(lib, D=256) == UNSUP
+    assert _chunk(lib, Sq=-1) == SHAPE
+    assert _chunk(lib, Skv=-1) == SHAPE
+    assert _chunk(lib, scale=0.0) == SHAPE
+    assert _chunk(lib, scale=float("nan")) == SHAPE
+    assert _chunk(lib, scale=float("inf")) == SHAPE
+    assert _chunk(lib, q=P + 2) == ALIGN
+    assert _chunk(lib, lse=P + 4) == ALIGN
+    assert _chunk(lib, qs=_st(0, 0, 129)) == ALIGN
+    assert _chunk(lib, os_=_st(0, 3, 128)) == ALIGN
+    assert _chunk(lib, ks=_st(-128, 0, 128)) == ALIGN
+    # fp32 strides need a multiple of 4 elements, bf16 a multiple of 8
+    assert _chunk(lib, in_dt=BF16, qs=_st(0, 0, 132)) == ALIGN
+    # empty problems are no-ops, even with NULL pointers
+    assert _chunk(lib, q=None, k=None, v=None, o=None, lse=None, Sq=0) == OK
+    assert _chunk(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == OK
+
+
+def test_lse_merge_argument_errors(attn):
+    lib = attn.load()
+    arr = (ctypes.c_void_p * 2)(P, P)
+    c = _st(2 * 10 * 128, 10 * 128, 128)
+    m = lambda n=2, op=arr, lp=arr, D=128, o=P, lse=P, odt=BF16, os_=c, Sq=10: lib.attn_lse_merge(
+        n, op, lp, 1, 2, Sq, D, o, os_, odt, lse, None)
+    assert m(n=0) == SHAPE
+    assert m(n=65) == UNSUP
+    assert m(D=32) == UNSUP
+    assert m(odt=5) == DTYPE
+    assert m(op=None) == NULL
+    assert m(o=None) == NULL
+    assert m(op=(ctypes.c_void_p * 2)(P, None)) == NULL
+    assert m(lp=(ctypes.c_void_p * 2)(P, P + 8)) == ALIGN
+    assert m(o=P + 2) == ALIGN
+    assert m(Sq=0, op=None, lp=None, o=None, lse=None) == OK
+
+
+def _shard(lib, lens=(10, 10), order=None, flags=4, ws=P, ws_bytes=1 << 30, D=128, q=P, in_dt=BF16, o_dt=BF16,
+           Sq=10):
+    c = _st(2 * 1000 * 128, 1000 * 128, 128)
+    n = len(lens)
+    la = (ctypes.c_int32 * max(n, 1))(*lens)
+    oa = None if order is None else (ctypes.c_int32 * len(order))(*order)
+    return lib.attn_shard_fwd(q, c, P, c, P, c, in_dt, 1, 2, Sq, D, 0.1, n, la, oa, flags, ws, ws_bytes, P, c, o_dt,
+                              P, None)
+
+
+def test_shard_fwd_argument_errors(attn):
+    lib = attn.load()
+    assert _shard(lib, lens=()) == SHAPE
+    assert _shard(lib, lens=(1,) * 65) == UNSUP
+    assert _shard(lib, lens=(10, -1)) == SHAPE
+    assert _shard(lib, lens=(2**30, 2**30)) == SHAPE
+    assert _shard(lib, order=(0, 0)) == SHAPE
+    assert _shard(lib, order=(0, 2)) == SHAPE
+    assert _shard(lib, order=(1, -1)) == SHAPE
+    assert _shard(lib, flags=0) == UNSUP
+    assert _shard(lib, flags=3) == UNSUP
+    assert _shard(lib, ws=None) == WS
+    need = lib.attn_shard_workspace_size(1, 2, 10, 128, 2, 4)
+    assert _shard(lib, ws_bytes=need - 1) == WS
+    assert _shard(lib, ws=P + 8, ws_bytes=need) == ALIGN
+    assert _shard(lib, D=80) == UNSUP
+    assert _shard(lib, q=None) == NULL
+    assert _shard(lib, in_dt=F32, o_dt=BF16) == DTYPE
+    assert _shard(lib, q=None, Sq=0) == OK
+
+
+def test_workspace_sizes(attn):
+    lib = attn.load()
+    rows = 1 * 16 * 5520
+    slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot   # n-way
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 2 * slot   # online
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == slot       # fused
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == 0
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0

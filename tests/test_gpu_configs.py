@@ -1,0 +1,155 @@
+"""GPU parity at the five workload shapes, in the launch configuration the bench times.
+
+At full size the oracle checks sampled query rows one by one (tile edges near
+both ends, rank boundaries, the last rows and seeded random rows, in every
+head).  Properties that hold at any size are checked on every row: all
+chunkings and merge schedules agree with the unchunked result, and the ring
+share equals the matching rows of the full sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import workloads
+from parity_util import assert_parity, errors, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_sequence_dit_amd import attn
+    attn.load()
+
+
+def A():
+    from long_sequence_dit_amd import attn
+    return attn
+
+
+class Case:
+    def __init__(self, w, n_random=48):
+        print("[case] %s: generating inputs" % w.name, flush=True)
+        self.w = w
+        self.host = w.make_inputs()
+        self.dev = {n: to_device(x) for n, x in self.host.items()}
+        bounds = [w.Sq * i // 8 for i in range(1, 8)]
+        self.rows = workloads.sample_rows(w.Sq, bounds, n_random=n_random)
+        print("[case] %s: oracle on %d rows x %d heads" % (w.name, len(self.rows), w.H), flush=True)
+        self.o_ref, self.l_ref = oracle.attention(self.host["q"], self.host["k"], self.host["v"], w.scale,
+                                                  q_rows=self.rows)
+
+    def run(self, plan_name=None, mode="fused"):
+        p = self.w.plan(plan_name)
+        o, l = A().shard_fwd(self.dev["q"], self.dev["k"], self.dev["v"], p.lens, p.order, mode=mode)
+        torch.cuda.synchronize()
+        return o, l
+
+    def check(self, o, l, what):
+        return assert_parity(o[:, :, self.rows], l[:, :, self.rows], self.o_ref, self.l_ref, what=what)
+
+    def free(self):
+        self.dev = None
+        torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def image_dit():
+    c = Case(workloads.IMAGE_DIT, n_random=96)
+    yield c
+    c.free()
+
+
+@pytest.fixture(scope="module")
+def ring_share():
+    c = Case(workloads.RING_SHARE)
+    yield c
+    c.free()
+
+
+@pytest.fixture(scope="module")
+def ulysses():
+    c = Case(workloads.ULYSSES_SHARE)
+    yield c
+    c.free()
+
+
+@pytest.fixture(scope="module")
+def full_seq():
+    c = Case(workloads.FULL_SEQUENCE, n_random=40)
+    yield c
+    c.free()
+
+
+def test_image_dit(image_dit):
+    o, l = image_dit.run()
+    image_dit.check(o, l, "image_dit")
+
+
+@pytest.mark.parametrize("mode", ["fused", "online", "nway"])
+def test_ring_share_modes(ring_share, mode):
+    o, l = ring_share.run(mode=mode)
+    ring_share.check(o, l, "ring_share %s" % mode)
+
+
+def test_ring_share_chunk_partials(ring_share):
+    c = ring_share
+    plan = c.w.plan()
+    off = 0
+    for ci, n in enumerate(plan.lens):
+        o, l = A().chunk_fwd(c.dev["q"], c.dev["k"][:, :, off:off + n], c.dev["v"][:, :, off:off + n], c.w.scale,
+                             out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        po, pl = oracle.attention(c.host["q"], c.host["k"], c.host["v"], c.w.scale, kv_range=(off, off + n),
+                                  q_rows=c.rows)
+        assert_parity(o[:, :, c.rows], l[:, :, c.rows], po, pl, what="ring partial chunk %d" % ci)
+        off += n
+
+
+def test_ring_share_other_rank():
+    w = workloads.ring_share(rank=5)
+    c = Case(w, n_random=16)
+    o, l = c.run()
+    c.check(o, l, "ring_share rank 5")
+    c.free()
+
+
+def test_ulysses_share(ulysses):
+    o, l = ulysses.run()
+    ulysses.check(o, l, "ulysses_share")
+
+
+PLANS = ["chunks1", "chunks2", "chunks4", "chunks8", "ragged", "ring8"]
+
+
+def test_full_sequence_plans_agree(full_seq):
+    o1, l1 = full_seq.run("chunks1")
+    full_seq.check(o1, l1, "full chunks1")
+    o1f, l1f = to_f64(o1), to_f64(l1)
+    for name in PLANS[1:]:
+        for mode in (("fused", "online", "nway") if name == "chunks8" else ("fused",)):
+            o, l = full_seq.run(name, mode)
+            full_seq.check(o, l, "full %s %s" % (name, mode))
+            # every row: the chunked result matches the unchunked one
+            mo, _ = errors(to_f64(o), o1f)
+            ml, _ = errors(to_f64(l), l1f)
+            print("  all rows vs chunks1: O %.3g LSE %.3g" % (mo, ml), flush=True)
+            assert mo <= 2e-2 and ml <= 2e-2
+
+
+def test_ring_share_equals_full_sequence_rows(ring_share):
+    # same seed, no outliers in the ring share: compare against a full-sequence run without outliers
+    w = workloads.Workload("full_no_outliers", 1, 16, 44160, 44160, 128, "bf16",
+                           plans={"c1": workloads.ChunkPlan((44160,))}, default_plan="c1")
+    x = w.make_inputs()
+    assert np.array_equal(x["k"], ring_share.host["k"])
+    qd = to_device(x["q"])
+    o, l = A().shard_fwd(qd, ring_share.dev["k"], ring_share.dev["v"], (44160,))
+    o_r, l_r = ring_share.run()
+    torch.cuda.synchronize()
+    mo, _ = errors(to_f64(o[:, :, :5520]), to_f64(o_r))
+    ml, _ = errors(to_f64(l[:, :, :5520]), to_f64(l_r))
+    assert mo <= 2e-2 and ml <= 2e-2, (mo, ml)

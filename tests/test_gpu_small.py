@@ -1,0 +1,202 @@
+"""GPU parity at sizes the oracle finishes in seconds: every output element is compared.
+
+Shapes span several query tiles (128 rows) and key tiles (64 rows) and end in
+ragged tails; edge cases cover empty chunks, -inf merges, strided layouts,
+the D = 64 path, fp32 partial outputs and bitwise repeatability.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads
+from parity_util import assert_parity, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_sequence_dit_amd import attn
+    attn.load()
+
+
+def A():
+    from long_sequence_dit_amd import attn
+    return attn
+
+
+def _inputs(B, H, Sq, Skv, D, kind=synth.KIND_BF16, seed=0, qk=1.0):
+    q = synth.normal_rows(seed, 0, B, H, Sq, D, factor=qk, kind=kind)
+    k = synth.normal_rows(seed, 1, B, H, Skv, D, factor=qk, kind=kind)
+    v = synth.normal_rows(seed, 2, B, H, Skv, D, kind=kind)
+    return q, k, v
+
+
+@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_chunk_fwd_all_elements(D, out):
+    B, H, Sq, Skv = 1, 3, 1000, 1500   # 1000 = 7*128 + 104, 1500 = 23*64 + 28
+    q, k, v = _inputs(B, H, Sq, Skv, D, qk=1.3)
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle.attention(q, k, v, scale)
+    od = torch.bfloat16 if out == "bf16" else torch.float32
+    o, l = A().chunk_fwd(to_device(q), to_device(k), to_device(v), scale, out_dtype=od)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="chunk_fwd D=%d out=%s" % (D, out))
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (31, 63), (33, 65), (129, 130), (128, 64), (257, 1)])
+def test_tails(Sq, Skv):
+    q, k, v = _inputs(2, 2, Sq, Skv, 128, seed=3)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(128))
+    o, l = A().chunk_fwd(to_device(q), to_device(k), to_device(v))
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="tails Sq=%d Skv=%d" % (Sq, Skv))
+
+
+def test_tiny_fp32_config_all_modes():
+    w = workloads.TINY
+    x = w.make_inputs()
+    q, k, v = (to_device(x[n]) for n in "qkv")
+    o_ref, l_ref = oracle.attention(x["q"], x["k"], x["v"], w.scale)
+    plan = w.plan()
+    for mode in ("nway", "online", "fused"):
+        o, l = A().shard_fwd(q, k, v, plan.lens, plan.order, mode=mode)
+        torch.cuda.synchronize()
+        assert_parity(o, l, o_ref, l_ref, fp32=True, what="tiny fp32 %s" % mode)
+    o, l = A().shard_fwd(q, k, v, (256,))
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, fp32=True, what="tiny fp32 unchunked")
+    # each chunk's partial against the oracle's partial over the same keys
+    parts = oracle.chunk_partials(x["q"], x["k"], x["v"], w.scale, plan.lens)
+    off = 0
+    gparts = []
+    for (po, pl), n in zip(parts, plan.lens):
+        o, l = A().chunk_fwd(q, k[:, :, off:off + n], v[:, :, off:off + n], w.scale)
+        torch.cuda.synchronize()
+        assert_parity(o, l, po, pl, fp32=True, what="tiny partial @%d" % off)
+        gparts.append((o, l))
+        off += n
+    # the standalone merge fed the oracle's partials rounded to fp32
+    po = [torch.from_numpy(p[0].astype(np.float32)).cuda() for p in parts]
+    pl = [torch.from_numpy(p[1].astype(np.float32)).cuda() for p in parts]
+    o, l = A().lse_merge(po, pl, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, fp32=True, what="merge of oracle partials")
+
+
+@pytest.mark.parametrize("mode", ["nway", "online", "fused"])
+def test_shard_modes_orders_and_empty_chunks(mode):
+    B, H, Sq, D = 1, 2, 300, 128
+    lens = (100, 0, 257, 1, 64, 0, 178)
+    q, k, v = _inputs(B, H, Sq, sum(lens), D, seed=5, qk=1.2)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    for order in (None, (6, 5, 4, 3, 2, 1, 0), (2, 0, 6, 1, 4, 5, 3)):
+        o, l = A().shard_fwd(qd, kd, vd, lens, order, mode=mode)
+        torch.cuda.synchronize()
+        assert_parity(o, l, o_ref, l_ref, what="shard %s order %s" % (mode, order))
+
+
+def test_bf16_chunk_partials_and_merge():
+    B, H, Sq, D = 1, 2, 200, 128
+    lens = (70, 130, 64)
+    q, k, v = _inputs(B, H, Sq, sum(lens), D, seed=6)
+    scale = 1 / math.sqrt(D)
+    parts = oracle.chunk_partials(q, k, v, scale, lens)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    off, go, gl = 0, [], []
+    for (po, pl), n in zip(parts, lens):
+        o, l = A().chunk_fwd(qd, kd[:, :, off:off + n], vd[:, :, off:off + n], scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert_parity(o, l, po, pl, what="bf16 partial @%d" % off)
+        go.append(o)
+        gl.append(l)
+        off += n
+    o_ref, l_ref = oracle.attention(q, k, v, scale)
+    o, l = A().lse_merge(go, gl, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="merge of GPU partials")
+    # ring-style in-place online merge: out aliases part 0
+    acc_o, acc_l = go[0].clone(), gl[0].clone()
+    for c in (1, 2):
+        A().lse_merge([acc_o, go[c]], [acc_l, gl[c]], out=acc_o, lse=acc_l)
+    torch.cuda.synchronize()
+    assert_parity(acc_o, acc_l, o_ref, l_ref, what="in-place online merge")
+
+
+def test_empty_chunk_and_minus_inf_merges():
+    B, H, Sq, D = 1, 2, 50, 64
+    q, k, v = _inputs(B, H, Sq, 40, D, seed=7)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, l = A().chunk_fwd(qd, kd[:, :, :0], vd[:, :, :0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+    o1, l1 = A().chunk_fwd(qd, kd, vd, out_dtype=torch.float32)
+    om, lm = A().lse_merge([o, o1, o], [l, l1, l], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(lm, l1)
+    assert torch.allclose(om, o1, rtol=0, atol=1e-7)
+    oe, le = A().lse_merge([o, o], [l, l], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(oe == 0) and torch.all(torch.isneginf(le)) and not torch.isnan(oe).any()
+    # a plan whose chunks are all empty
+    oz, lz = A().shard_fwd(qd, kd[:, :, :0], vd[:, :, :0], (0, 0), mode="nway")
+    torch.cuda.synchronize()
+    assert torch.all(oz == 0) and torch.all(torch.isneginf(lz))
+
+
+def test_strided_bshd_views():
+    B, S, H, D = 2, 333, 3, 128
+    rng = np.random.default_rng(1)
+    base = [synth.f32_to_bf16_bits(rng.standard_normal((B, S, H, D)).astype(np.float32)) for _ in range(3)]
+    qd, kd, vd = (to_device(x).permute(0, 2, 1, 3) for x in base)  # [B,H,S,D] views of [B,S,H,D]
+    out = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
+    qh, kh, vh = (np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in base)
+    o_ref, l_ref = oracle.attention(qh, kh, vh, 1 / math.sqrt(D))
+    o, l = A().chunk_fwd(qd, kd, vd, out=out)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="strided chunk_fwd")
+    out2 = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
+    o, l = A().shard_fwd(qd, kd, vd, (100, 233), (1, 0), mode="fused", out=out2)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="strided shard_fwd")
+
+
+def test_uniform_values_and_determinism():
+    B, H, Sq, Skv, D = 1, 2, 256, 700, 128
+    q, k, _ = _inputs(B, H, Sq, Skv, D, seed=8, qk=1.5)
+    row = synth.f32_to_bf16_bits(np.linspace(-2, 2, D).astype(np.float32))
+    v = np.broadcast_to(row, (B, H, Skv, D)).copy()
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, l = A().chunk_fwd(qd, kd, vd, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = synth.bf16_bits_to_f32(row).astype(np.float64)
+    err = np.abs(to_f64(o) - want).max()
+    assert err <= 2e-2 * np.abs(want).max(), err
+    o2, l2 = A().chunk_fwd(qd, kd, vd, out_dtype=torch.float32)
+    o3, l3 = A().shard_fwd(qd, kd, vd, (300, 400), mode="fused", out_dtype=torch.float32)
+    o4, l4 = A().shard_fwd(qd, kd, vd, (300, 400), mode="fused", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(l, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
+
+
+def test_noop_and_nonfinite_inputs():
+    D = 128
+    qd = torch.empty((1, 2, 0, D), dtype=torch.bfloat16, device="cuda")
+    kd = torch.zeros((1, 2, 10, D), dtype=torch.bfloat16, device="cuda")
+    o, l = A().chunk_fwd(qd, kd, kd)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, D)
+    q, k, v = _inputs(1, 1, 64, 64, D, seed=9)
+    v[0, 0, 5, 7] = 0x7FC0  # a NaN in V propagates to every output of that column
+    o, l = A().chunk_fwd(to_device(q), to_device(k), to_device(v), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0, 0, :, 7]).all() and torch.isfinite(l).all()
