@@ -42,7 +42,9 @@
  *    yields O = 0 and LSE = -inf (no NaN).  Non-finite inputs propagate.
  *  - Supported: D in {64, 128}; input dtype bf16 (MFMA path, fp32
  *    accumulation) or fp32 (fp32 throughout); output dtype bf16 or fp32 for
- *    bf16 inputs, fp32 for fp32 inputs.
+ *    bf16 inputs, fp32 for fp32 inputs.  For bf16 inputs one head's key and
+ *    value rows must span less than 2 GiB: (Skv + 64) * s-stride * 2 bytes
+ *    < 2^31 (ATTN_ERR_UNSUPPORTED otherwise).
  */
 #ifndef LSDIT_ATTN_H
 #define LSDIT_ATTN_H

@@ -61,6 +61,10 @@ attn_status_t check_common(const void* q, attn_strides_t qs, const void* k, attn
     if (Skv != 0) {
         if (!aligned16(k) || !aligned16(v)) return ATTN_ERR_ALIGN;
         if (!strides_ok(ks, ie) || !strides_ok(vs, ie)) return ATTN_ERR_ALIGN;
+        // the bf16 kernel addresses one head's K/V rows with 32-bit byte offsets
+        const int64_t lim = (int64_t)1 << 31;
+        if (in_dt == ATTN_BF16 && ((int64_t)(Skv + 256) * ks.s * 2 >= lim || (int64_t)(Skv + 256) * vs.s * 2 >= lim))
+            return ATTN_ERR_UNSUPPORTED;
     }
     return ATTN_OK;
 }

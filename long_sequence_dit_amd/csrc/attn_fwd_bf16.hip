@@ -9,12 +9,10 @@
 // Attention").  Optionally the epilogue merges the result into a running
 // fp32 (O, LSE) by log-sum-exp weights.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition: one workgroup = 8 waves = 256 query rows of one head,
+// one workgroup per CU (two waves per SIMD).
 //  * each wave owns 32 query rows; its Q rows stay in VGPRs for the whole
 //    key loop as the B operand of v_mfma_f32_32x32x16_bf16;
-//  * key tiles of 64 rows of K and V go HBM -> VGPR staging -> LDS, double
-//    buffered, with 16-byte coalesced loads; the next tile's loads are in
-//    flight while the current tile is computed;
 //  * scores are computed transposed, S^T = K Q^T, so every lane holds 32
 //    scores of ONE query row (lanes l and l+32 share a row); row max and row
 //    sum are in-lane plus one permlane32 swap;
@@ -22,7 +20,26 @@
 //    B operand of O^T += V^T P^T.  The MFMA k index is a relabelling of the
 //    keys, so V^T is read from the row-major V tile with ds_read_b64_tr_b16
 //    at the matching key rows;
-//  * exponentials are base 2 with scale*log2(e) folded into one FMA.
+//  * per 64-key tile t a wave runs one hand-ordered stream of MFMA slots:
+//    the P.V MFMAs of tile t-1, then the score MFMAs of tile t+1.  Each slot
+//    also issues the LDS read of the operand kPrefetch slots ahead, and the
+//    slots carry a fixed share of the softmax of tile t: the max tree, then
+//    the probabilities as a three-stage software pipeline (FMA, exp, pack
+//    and sum in consecutive slots), so no slot holds a dependent VALU chain
+//    that would stall the wave's next MFMA, and the scores of tile t are dead
+//    before those of tile t+1 are born.  Scheduling barriers pin this order:
+//    left to itself the compiler moves each LDS read next to its MFMA
+//    (exposing the LDS latency on every MFMA) and bunches the MFMAs apart
+//    from the VALU;
+//  * K/V tiles of 64 rows go HBM -> LDS directly (buffer loads with the LDS
+//    destination) into three buffers each, K issued two iterations and V
+//    one iteration before use, through buffer resources whose out-of-range
+//    rows read as zero (and are masked); LDS rows are XOR swizzled in
+//    16-byte chunks so both the row reads of K and the transposed reads of V
+//    are free of bank conflicts;
+//  * exponentials are base 2 with scale*log2(e) folded into one FMA; the
+//    running output is rescaled only when a row maximum grows by more than
+//    2^8.
 // Workgroups are remapped so that each XCD (workgroups are dealt to the 8
 // XCDs round-robin) runs consecutive query tiles of the same head, which
 // then share K/V tiles in that XCD's L2.
@@ -39,28 +56,52 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int kPrefetch = 4;      // MFMA operands read this many slots ahead
 
 template <int D>
 struct Cfg {
-    static constexpr int NW = 4;                 // waves per workgroup
-    static constexpr int NT = NW * 64;           // threads per workgroup
-    static constexpr int BQ = 32 * NW;           // query rows per workgroup
-    static constexpr int BK = 64;                // keys per tile
-    static constexpr int LDK = D + 8;            // K row pitch (elements): conflict-free 16 B row reads
-    static constexpr int LDV = D + 32;           // V row pitch: conflict-free transposed 8 B reads
-    static constexpr int K_ELEMS = BK * LDK;
-    static constexpr int V_ELEMS = BK * LDV;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;
-    static constexpr int CHUNKS = D / 8;         // 16-byte chunks per row
-    static constexpr int LOADS = BK * CHUNKS / NT;  // 16-byte loads per thread per tensor per tile
-    static_assert(BK * CHUNKS % NT == 0, "tile must split evenly over the threads");
+    static constexpr int NW = 8;                  // waves per workgroup
+    static constexpr int NT = NW * 64;            // threads per workgroup
+    static constexpr int BQ = 32 * NW;            // query rows per workgroup
+    static constexpr int BK = 64;                 // keys per tile
+    static constexpr int CH = D / 8;              // 16-byte chunks per row
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int TILE_BYTES = BK * ROW_BYTES;
+    static constexpr int NSTAGE = 3;                        // LDS buffers per tensor
+    static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;
+    static constexpr int ROWS_PER_BLK = 64 / CH;            // rows one wave-wide 1 KiB load covers
+    static constexpr int BLKS = BK / ROWS_PER_BLK;          // 1 KiB blocks per tile
+    static constexpr int BLKS_PER_WAVE = BLKS / NW;
+    static_assert(BLKS % NW == 0, "tile must split evenly over the waves");
+    static constexpr int N_PV = (D / 32) * 4;               // P.V slots: (ks, dt), dt fastest
+    static constexpr int N_S = (D / 16) * 2;                // score slots: (kk, kb), kb fastest
 };
+
+// XOR swizzles of the 16-byte chunk index within a row (bijections on 0..CH-1).
+// K: lanes reading consecutive rows at one chunk land in distinct bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row & 7) ^ ((row >> 3) & 1);
+}
+// V: a wave's transposed reads touch 4 consecutive rows (row & 3) and, per
+// 16 lanes, two neighbouring chunks; these masks spread them over the banks.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+    const int s0 = row & 1, s1 = (row >> 1) & 1;
+    if constexpr (D == 128) return 10 * s0 + 4 * s1;
+    else return 2 * s0 + 4 * s1;
+}
 
 // Workgroups are dispatched to the 8 XCDs round-robin; give XCD x a contiguous
 // range of logical tiles so its concurrently resident workgroups share K/V.
@@ -87,12 +128,237 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-template <int D>
-__global__ __launch_bounds__(Cfg<D>::NT, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt, float c) {
-    using C = Cfg<D>;
-    extern __shared__ __attribute__((aligned(16))) unsigned short smem[];
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Buffer resource of a K or V head: base, no stride, num_records bytes; reads past the
+// end return zeros.
+struct Rsrc {
+    i32x4_t w;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
+    const unsigned long long a = (unsigned long long)base;
+    Rsrc r;
+    r.w[0] = (int)(unsigned)a;
+    r.w[1] = (int)((unsigned)(a >> 32) & 0xFFFFu);
+    r.w[2] = num_records;
+    r.w[3] = 0x00020000;
+    return r;
+}
+
+// NB wave-wide 16-byte-per-lane loads into consecutive 1 KiB LDS blocks at LDS byte address
+// dst.  Written as assembly on purpose: for the builtin form the compiler assumes that any
+// later LDS read may read what the load writes, and waits for the load to land before the
+// next ds_read — which would expose the whole load latency in every iteration of the key
+// loop.  Here the kernel orders these writes itself (an explicit vmcnt wait, then a
+// barrier, before any wave reads the buffer).  The loads have no register results, so
+// nothing the compiler allocates is written while they are in flight.  M0 holds the LDS
+// address; one wait state separates its write from the load that uses it.
+template <int NB>
+__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB], int soff) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            :
+            : "s"(dst + i * 1024u), "v"(goff[i]), "s"(rs.w), "s"(soff)
+            : "memory", "m0");
+}
+
+// Per-wave state of the key loop.
+template <int D>
+struct Wave {
+    f32x16_t acc[D / 32];  // O^T accumulators
+    bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
+    float m_run;           // reference max (scaled, log2 domain)
+    float l_run;           // this lane's share of the running row sum
+    int k_base, v_base;    // per-lane LDS read offsets (see the kernel)
+    float c;               // scale * log2(e)
+};
+
+// Element f (0..31) of a lane's score tile (f is a compile-time constant after unrolling).
+__device__ __forceinline__ float sel_f(const f32x16_t (&s)[2], int f) { return s[f >> 4][f & 15]; }
+
+// Softmax state carried across the slots of one stream.
+struct Soft {
+    float mt[11];           // partial maxima
+    float m0, m1;           // row max of each half of the wave
+    float m_new, alpha, rs0, rs1;
+    float x[16][2];         // stage A results (scaled, shifted scores)
+    float e[16][2];         // stage B results (probabilities)
+};
+
+// Positions of the softmax work in a stream.  The max tree takes slots 0..4; probability
+// pair J (scores 2J, 2J+1 -> word J%4 of p[J/4]) then runs as a 3-stage pipeline: A (two
+// FMAs) at slot a(J), B (two exps) at a(J)+1, C (pack, sums) at a(J)+2, with a(J) spread
+// evenly over 5..LA.  So every slot's VALU ops are independent of each other (a dependent
+// chain inside a slot would hold up the wave's next MFMA, since a wave issues in order),
+// and with LA the last P.V slot, all reads of the scores finish before the score MFMAs of
+// the next tile overwrite them.
+__host__ __device__ constexpr int pair_slot(int j, int la) { return 5 + j * (la - 4) / 16; }
+
+// Empty asm statements (register operands only) pin a stage to its slot: the scheduling
+// barriers order instructions, but pure arithmetic could still be hoisted above them or
+// sunk towards its use.
+__device__ __forceinline__ void pin(float& a, float& b) { asm volatile("" : "+v"(a), "+v"(b)); }
+
+template <int POS, int LA, int J = 0>
+__device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&s)[2], u32x4_t (&p)[4]) {
+    if constexpr (J < 16) {
+        constexpr int a = pair_slot(J, LA);
+        if constexpr (POS == a) {
+            float x0 = s[J >> 3][2 * (J & 7)], x1 = s[J >> 3][2 * (J & 7) + 1];
+            pin(x0, x1);
+            sm.x[J][0] = __builtin_fmaf(x0, c, -sm.m_new);
+            sm.x[J][1] = __builtin_fmaf(x1, c, -sm.m_new);
+            pin(sm.x[J][0], sm.x[J][1]);
+        } else if constexpr (POS == a + 1) {
+            sm.e[J][0] = fast_exp2(sm.x[J][0]);
+            sm.e[J][1] = fast_exp2(sm.x[J][1]);
+            pin(sm.e[J][0], sm.e[J][1]);
+        } else if constexpr (POS == a + 2) {
+            unsigned word = pack_bf16(sm.e[J][0], sm.e[J][1]);
+            float& rs = (J & 1) ? sm.rs1 : sm.rs0;
+            rs += sm.e[J][0] + sm.e[J][1];
+            asm volatile("" : "+v"(word), "+v"(rs));
+            p[J >> 2][J & 3] = word;
+        }
+        pair_stages<POS, LA, J + 1>(c, sm, s, p);
+    }
+}
+
+// The share of the softmax of s that stream position POS carries.
+template <int D, int POS>
+__device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_t (&s)[2], u32x4_t (&p)[4]) {
+    if constexpr (POS == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
+    } else if constexpr (POS == 1) {
+#pragma unroll
+        for (int i = 4; i < 8; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
+    } else if constexpr (POS == 2) {
+        sm.mt[8] = max3(sel_f(s, 24), sel_f(s, 25), sel_f(s, 26));
+        sm.mt[9] = max3(sel_f(s, 27), sel_f(s, 28), sel_f(s, 29));
+        sm.mt[10] = fmaxf(sel_f(s, 30), sel_f(s, 31));
+        sm.mt[0] = max3(sm.mt[0], sm.mt[1], sm.mt[2]);
+        sm.mt[1] = max3(sm.mt[3], sm.mt[4], sm.mt[5]);
+    } else if constexpr (POS == 3) {
+        const float mx = max3(max3(sm.mt[0], sm.mt[1], sm.mt[6]), max3(sm.mt[7], sm.mt[8], sm.mt[9]), sm.mt[10]);
+        half_pair(mx, sm.m0, sm.m1);
+    } else if constexpr (POS == 4) {
+        // Lazy rescale: a row's reference max only moves when the row's max exceeds it by
+        // more than kRescale (log2 units).  Weights are then at most 2^kRescale, harmless in
+        // fp32 and bf16, and O and l stay consistent because both use the same reference.
+        // Lanes l and l+32 hold the same row and take the same decision.
+        const float m_tile = fmaxf(sm.m0, sm.m1) * w.c;
+        sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
+        sm.alpha = fast_exp2(w.m_run - sm.m_new);
+        w.m_run = sm.m_new;
+        sm.rs0 = 0.f;
+        sm.rs1 = 0.f;
+    }
+    pair_stages<POS, Cfg<D>::N_PV - 1>(w.c, sm, s, p);
+}
+
+// All softmax positions in order (for a tile whose softmax runs on its own).
+template <int D, int POS = 0>
+__device__ __forceinline__ void softmax_all(Wave<D>& w, Soft& sm, const f32x16_t (&s)[2], u32x4_t (&p)[4]) {
+    if constexpr (POS < Cfg<D>::N_PV + 2) {
+        softmax_slot<D, POS>(w, sm, s, p);
+        softmax_all<D, POS + 1>(w, sm, s, p);
+    }
+}
+
+// One MFMA operand (16 bytes) of stream slot SLOT.  vb / kb are this lane's read offsets
+// with the buffer's LDS offset OR-ed in (buffers are tile-aligned, so the swizzled low bits
+// are untouched); XOR-ing the slot constant into that loop-variant value keeps the compiler
+// from hoisting a table of loop-invariant addresses out of the key loop (and spilling it).
+template <int D, int SLOT>
+__device__ __forceinline__ u32x4_t read_opnd(const lds_u8_t* lds, int vb, int kb_) {
+    using C = Cfg<D>;
+    if constexpr (SLOT < C::N_PV) {
+        constexpr int ks = SLOT / (D / 32), dt = SLOT % (D / 32);
+        const lds_u8_t* base = lds + (vb ^ (dt << 6)) + 16 * ks * C::ROW_BYTES;
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)base));
+        const u32x2_t hi =
+            __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 8 * C::ROW_BYTES)));
+        return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+        constexpr int sl = SLOT - C::N_PV, kk = sl >> 1, kb = sl & 1;
+        return *(const lds_u32x4_t*)(lds + (kb_ ^ (kk << 5)) + kb * 32 * C::ROW_BYTES);
+    }
+}
+
+// Slot SLOT of a stream (see stream()), then the following slots.
+template <int D, bool DO_PV, bool DO_S, bool DO_SM, int SLOT>
+__device__ __forceinline__ void stream_slots(Wave<D>& w, const lds_u8_t* lds, int vb, int kb_, u32x4_t (&ring)[kPrefetch],
+                                             const u32x4_t (&p_prev)[4], f32x16_t (&s)[2], u32x4_t (&p_cur)[4],
+                                             Soft& sm) {
+    using C = Cfg<D>;
+    constexpr int first = DO_PV ? 0 : C::N_PV;
+    constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
+    if constexpr (SLOT < last) {
+        constexpr int pos = SLOT - first;
+        const u32x4_t op = ring[pos % kPrefetch];
+        if constexpr (SLOT < C::N_PV) {
+            constexpr int ks = SLOT / (D / 32), dt = SLOT % (D / 32);
+            w.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
+                                                                __builtin_bit_cast(bf16x8_t, p_prev[ks]), w.acc[dt],
+                                                                0, 0, 0);
+        } else {
+            constexpr int sl = SLOT - C::N_PV, kk = sl >> 1, kb = sl & 1;
+            if constexpr (kk == 0) {
+                const f32x16_t zero = {};
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op), w.qf[kk], zero, 0,
+                                                                0, 0);
+            } else {
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op), w.qf[kk], s[kb], 0,
+                                                                0, 0);
+            }
+        }
+        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(lds, vb, kb_);
+        if constexpr (DO_SM && pos < C::N_PV + 2) softmax_slot<D, pos>(w, sm, s, p_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, lds, vb, kb_, ring, p_prev, s, p_cur, sm);
+    }
+}
+
+template <int D, bool DO_PV, int I = 0>
+__device__ __forceinline__ void ring_fill(const lds_u8_t* lds, int vb, int kb_, u32x4_t (&ring)[kPrefetch], int last) {
+    using C = Cfg<D>;
+    constexpr int first = DO_PV ? 0 : C::N_PV;
+    if constexpr (I < kPrefetch) {
+        if (first + I < last) ring[I] = read_opnd<D, first + I>(lds, vb, kb_);
+        ring_fill<D, DO_PV, I + 1>(lds, vb, kb_, ring, last);
+    }
+}
+
+// One stream: P.V of the tile at LDS offset v0 (if DO_PV, with probabilities p_prev), the
+// softmax of the scores in s into p_cur (if DO_SM; on the P.V slots), then the scores of the
+// tile at k0 into s (if DO_S; on the later slots, after the softmax has read s).
+template <int D, bool DO_PV, bool DO_S, bool DO_SM>
+__device__ __forceinline__ void stream(Wave<D>& w, const lds_u8_t* lds, int v0, int k0, const u32x4_t (&p_prev)[4],
+                                       f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
+    using C = Cfg<D>;
+    static_assert(!DO_SM || (DO_PV && DO_S), "the softmax needs the full stream's slots");
+    static_assert(C::N_PV >= 8 && C::N_S >= 2, "stream too short for the softmax pipeline");
+    constexpr int first = DO_PV ? 0 : C::N_PV;
+    constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
+    const int vb = w.v_base | v0, kb_ = w.k_base | k0;
+    u32x4_t ring[kPrefetch];
+    ring_fill<D, DO_PV>(lds, vb, kb_, ring, last);
+    __builtin_amdgcn_sched_barrier(0);
+    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, lds, vb, kb_, ring, p_prev, s, p_cur, sm);
+}
+
+template <int D>
+__global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int n_qt, float c) {
+    using C = Cfg<D>;
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5;  // which half of the wave (MFMA k-half)
     const int tile = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = tile / n_qt, qt = tile % n_qt;
@@ -102,155 +368,154 @@ __global__ __launch_bounds__(Cfg<D>::NT, 2) void fwd_bf16_kernel(FwdArgs a, int 
     const unsigned short* kp = (const unsigned short*)a.k + b * a.ks.b + h * a.ks.h;
     const unsigned short* vp = (const unsigned short*)a.v + b * a.vs.b + h * a.vs.h;
     const int Skv = a.Skv;
+    const int nkt = (Skv + C::BK - 1) / C::BK;
+
+    Wave<D> w;
+    w.c = c;
+    w.m_run = -INFINITY;
+    w.l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
 
     // ---- Q fragments: B operand, lane holds Q[row][16kk + 8hi .. +8]
     const int qrow = qt * C::BQ + wave * 32 + (lane & 31);
     const int qrow_c = qrow < a.Sq ? qrow : a.Sq - 1;
-    bf16x8_t qf[D / 16];
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk)
-        qf[kk] = *(const bf16x8_t*)(qp + (int64_t)qrow_c * a.qs.s + 16 * kk + 8 * hi);
+        w.qf[kk] = *(const bf16x8_t*)(qp + (int64_t)qrow_c * a.qs.s + 16 * kk + 8 * hi);
 
-    f32x16_t acc[D / 32];
+    // ---- K/V loads straight into LDS.  One wave-wide instruction fills a contiguous
+    // 1 KiB block (lane L -> bytes 16L..16L+15); lane L fetches the global chunk that the
+    // swizzle maps to its slot.  Offsets are per lane and fixed; tiles advance by a scalar.
+    // Loads of tiles past the chunk fall outside the buffer and read zeros.
+    const int k_rs = (int)(a.ks.s * 2), v_rs = (int)(a.vs.s * 2);  // row pitch in bytes
+    const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D * 2);
+    const Rsrc vrs = make_rsrc(vp, (Skv - 1) * v_rs + D * 2);
+    int k_goff[C::BLKS_PER_WAVE], v_goff[C::BLKS_PER_WAVE];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-    float m_run = -INFINITY;  // running max of scale*log2(e)*s
-    float l_run = 0.f;        // this lane's share of the running row sum
-
-    const int nkt = (Skv + C::BK - 1) / C::BK;
-    u32x4_t kst[C::LOADS], vst[C::LOADS];
-
-    auto gload = [&](int t) {
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int idx = tid + i * C::NT;
-            const int row = idx / C::CHUNKS, ch = idx % C::CHUNKS;
-            int key = t * C::BK + row;
-            key = key < Skv ? key : Skv - 1;
-            kst[i] = *(const u32x4_t*)(kp + (int64_t)key * a.ks.s + ch * 8);
-            vst[i] = *(const u32x4_t*)(vp + (int64_t)key * a.vs.s + ch * 8);
-        }
+    for (int i = 0; i < C::BLKS_PER_WAVE; ++i) {
+        const int blk = wave * C::BLKS_PER_WAVE + i;
+        const int row = blk * C::ROWS_PER_BLK + lane / C::CH, slot = lane % C::CH;
+        k_goff[i] = row * k_rs + (slot ^ k_swz<D>(row)) * 16;
+        v_goff[i] = row * v_rs + (slot ^ v_swz<D>(row)) * 16;
+    }
+    lds_u8_t* const lds = (lds_u8_t*)smem;
+    const unsigned lds_base = (unsigned)(size_t)lds;  // LDS byte address of the tile block
+    // LDS byte offsets of the tile buffers (the dynamic LDS block starts at offset 0)
+    auto kbuf = [&](int t) { return (t % C::NSTAGE) * C::TILE_BYTES; };
+    auto vbuf = [&](int t) { return (C::NSTAGE + t % C::NSTAGE) * C::TILE_BYTES; };
+    auto load_k = [&](int t) {
+        lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(t) + wave * C::BLKS_PER_WAVE * 1024, k_goff, t * C::BK * k_rs);
     };
-    auto swrite = [&](int buf) {
-        unsigned short* Ks = smem + buf * C::BUF_ELEMS;
-        unsigned short* Vs = Ks + C::K_ELEMS;
-#pragma unroll
-        for (int i = 0; i < C::LOADS; ++i) {
-            const int idx = tid + i * C::NT;
-            const int row = idx / C::CHUNKS, ch = idx % C::CHUNKS;
-            *(u32x4_t*)(Ks + row * C::LDK + ch * 8) = kst[i];
-            *(u32x4_t*)(Vs + row * C::LDV + ch * 8) = vst[i];
-        }
+    auto load_v = [&](int t) {
+        lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(t) + wave * C::BLKS_PER_WAVE * 1024, v_goff, t * C::BK * v_rs);
     };
 
-    gload(0);
-    swrite(0);
-    __syncthreads();
+    // ---- per-lane LDS read offsets (bytes, within a buffer).  Each swizzle XOR only touches
+    // chunk-index bits that the loop index sets independently, so one per-lane base XOR-ed
+    // with a compile-time constant addresses every operand; row steps are additive.
+    // K operand (kb, kk): row kb*32 + (lane&31), chunk 2kk + hi  ->  k_base ^ (kk << 5)
+    // (k_swz(row + 32) == k_swz(row)).
+    w.k_base = (lane & 31) * C::ROW_BYTES + ((hi ^ k_swz<D>(lane & 31)) * 16);
+    // V^T operand (dt, ks, lo/hi): rows 16ks + 4(g>>1) + (j>>2) (+8), element columns
+    // 32dt + 16(g&1) + 4(j&3)  ->  v_base ^ (dt << 6); v_swz depends on row & 3 only.
+    {
+        const int g = lane >> 4, j = lane & 15;
+        const int v_row0 = 4 * (g >> 1) + (j >> 2);
+        const int v_col0 = 16 * (g & 1) + 4 * (j & 3);
+        w.v_base = v_row0 * C::ROW_BYTES + (((v_col0 >> 3) ^ v_swz<D>(v_row0)) * 16) + (v_col0 & 7) * 2;
+    }
 
-    // transposed-read addressing for the V^T operand (see header comment)
-    const int g = lane >> 4, j = lane & 15;
-    const int v_row0 = 4 * (g >> 1) + (j >> 2);
-    const int v_col0 = 16 * (g & 1) + 4 * (j & 3);
-
-    for (int t = 0; t < nkt; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nkt) gload(t + 1);
-        const unsigned short* Ks = smem + buf * C::BUF_ELEMS;
-        const unsigned short* Vs = Ks + C::K_ELEMS;
-
-        // ---- S^T = K Q^T for 2 blocks of 32 keys
-        f32x16_t s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const bf16x8_t kf = *(const bf16x8_t*)(Ks + (kb * 32 + (lane & 31)) * C::LDK + 16 * kk + 8 * hi);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
-            }
-        }
-        // ---- mask keys past the end of the chunk (last tile only)
+    // Key of accumulator element (kb, r) is kb*32 + 8(r>>2) + 4hi + (r&3); compare its
+    // compile-time part against valid - 4hi, so no table of per-lane key indices is kept live.
+    auto mask = [&](f32x16_t(&s)[2], int t) {
         const int valid = Skv - t * C::BK;
         if (valid < C::BK) {
+            const int lim = valid - 4 * hi;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    if (key >= valid) s[kb][r] = -INFINITY;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
         }
-        // ---- online softmax (base 2, scaled domain)
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        float m0, m1;
-        half_pair(mx, m0, m1);
-        const float m_new = fmaxf(m_run, fmaxf(m0, m1) * c);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(__builtin_fmaf(s[kb][r], c, -m_new));
-                s[kb][r] = p;
-                rs += p;
-            }
-        l_run = l_run * alpha + rs;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    };
 
-        // ---- P^T as bf16 B operands: (kb, st) covers accumulator regs 8st..8st+7 of block kb
-        bf16x8_t pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                u32x4_t w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = pack_bf16(s[kb][8 * st + 2 * e], s[kb][8 * st + 2 * e + 1]);
-                pf[kb * 2 + st] = __builtin_bit_cast(bf16x8_t, w);
-            }
+    // ---- prologue.  Zero the tiles first: key rows past the end of a chunk are masked
+    // (P = 0), and zeros there keep 0 * V finite whatever the loads leave in those rows.
+    for (int i = tid; i < C::LDS_BYTES / 16; i += C::NT) ((lds_u32x4_t*)lds)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+    load_k(0);
+    load_k(1);
+    load_k(2);
+    load_v(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles are in
+    __syncthreads();
 
-        // ---- O^T += V^T P^T
+    f32x16_t sc[2];      // scores: of tile t while its softmax runs, then of tile t+1
+    u32x4_t pA[4], pB[4];  // probabilities of alternate tiles
+    Soft sm;
+    // after the softmax of a tile: running sum, and the rare rescale of the running output
+    auto finish_softmax = [&]() {
+        w.l_run = w.l_run * sm.alpha + (sm.rs0 + sm.rs1);
+        if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const unsigned short* base = Vs + (16 * ks + v_row0) * C::LDV + 32 * dt + v_col0;
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)base);
-                const i16x4_t hi8 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 8 * C::LDV));
-                u32x4_t w;
-                const u32x2_t wl = __builtin_bit_cast(u32x2_t, lo), wh = __builtin_bit_cast(u32x2_t, hi8);
-                w[0] = wl[0];
-                w[1] = wl[1];
-                w[2] = wh[0];
-                w[3] = wh[1];
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pf[ks], acc[dt],
-                                                                  0, 0, 0);
-            }
+                for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
         }
+    };
+    // tile 0: scores, then its softmax on its own
+    stream<D, false, true, false>(w, lds, vbuf(0), kbuf(0), pB, sc, pB, sm);  // S_0
+    mask(sc, 0);
+    softmax_all<D>(w, sm, sc, pA);  // P_0 -> pA
+    finish_softmax();
+    __syncthreads();  // every wave is done with K buffer 0 before tile 3 overwrites it
 
-        if (t + 1 < nkt) swrite(buf ^ 1);
+    // ---- key loop.  Iteration t: issue K_{t+3} (into K_t's buffer) and V_{t+1} (into
+    // V_{t-2}'s buffer); stream P.V of tile t-1 with the softmax of tile t, then the scores of
+    // tile t+1; then wait for the previous iteration's loads (K_{t+2}, V_t) and sync.  K_t is
+    // read in iteration t-1 (scores) and V_t in iteration t+1 (P.V), each before the barrier
+    // that precedes its buffer's refill.  Scores of tile nkt are computed from a stale buffer
+    // and never used.  The probability registers swap roles every iteration (pA <-> pB).
+    constexpr int kWaitPrev = 0x0F70 | (2 * C::BLKS_PER_WAVE);  // vmcnt(loads issued this iteration)
+    auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4]) {
+        load_k(t + 3);
+        load_v(t + 1);
+        if (t == 0) {
+            stream<D, false, true, false>(w, lds, vbuf(0), kbuf(1), p_prev, sc, p_cur, sm);
+        } else {
+            stream<D, true, true, true>(w, lds, vbuf(t - 1), kbuf(t + 1), p_prev, sc, p_cur, sm);
+            finish_softmax();
+        }
+        if (t + 1 < nkt) mask(sc, t + 1);
+        __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
+    };
+    iter(0, pB, pA);  // scores S_1
+    int t = 1;
+    for (; t + 1 < nkt; t += 2) {
+        iter(t, pA, pB);      // P.V with P_{t-1} = pA, softmax S_t -> pB
+        iter(t + 1, pB, pA);  // P.V with P_t = pB, softmax S_{t+1} -> pA
     }
+    if (t < nkt) {
+        iter(t, pA, pB);
+        ++t;
+    }
+    // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)
+    if (nkt & 1)
+        stream<D, true, false, false>(w, lds, vbuf(nkt - 1), kbuf(0), pA, sc, pB, sm);
+    else
+        stream<D, true, false, false>(w, lds, vbuf(nkt - 1), kbuf(0), pB, sc, pA, sm);
 
     // ---- epilogue: normalise, LSE, optional merge into the running result, store
     float l0, l1;
-    half_pair(l_run, l0, l1);
+    half_pair(w.l_run, l0, l1);
     const float l_tot = l0 + l1;
     const float inv_l = 1.f / l_tot;
-    float lse2 = m_run + log2f(l_tot);  // log2 domain
-    float wa = 0.f, wb = inv_l;          // out = wa * prev + wb * acc
+    float lse2 = w.m_run + log2f(l_tot);  // log2 domain
+    float wa = 0.f, wb = inv_l;            // out = wa * prev + wb * acc
     const int64_t lrow = (int64_t)bh * a.Sq + qrow;
     if (a.prev_o != nullptr && qrow < a.Sq) {
         const float lp = a.prev_lse[lrow] * kLog2e;
@@ -272,16 +537,16 @@ __global__ __launch_bounds__(Cfg<D>::NT, 2) void fwd_bf16_kernel(FwdArgs a, int 
                     const int d = 32 * dt + 8 * r4 + 4 * hi;
                     float x[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * r4 + e] * wb;
+                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * wb;
                     if (pp) {
                         const f32x4_t pv = *(const f32x4_t*)(pp + d);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) x[e] += wa * pv[e];
                     }
-                    u32x2_t w;
-                    w[0] = pack_bf16(x[0], x[1]);
-                    w[1] = pack_bf16(x[2], x[3]);
-                    *(u32x2_t*)(op + d) = w;
+                    u32x2_t wd;
+                    wd[0] = pack_bf16(x[0], x[1]);
+                    wd[1] = pack_bf16(x[2], x[3]);
+                    *(u32x2_t*)(op + d) = wd;
                 }
         } else {
             float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
@@ -292,7 +557,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 2) void fwd_bf16_kernel(FwdArgs a, int 
                     const int d = 32 * dt + 8 * r4 + 4 * hi;
                     f32x4_t x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = acc[dt][4 * r4 + e] * wb;
+                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * wb;
                     if (pp) {
                         const f32x4_t pv = *(const f32x4_t*)(pp + d);
 #pragma unroll

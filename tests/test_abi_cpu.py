@@ -85,6 +85,11 @@ def test_chunk_fwd_argument_errors(attn):
     assert _chunk(lib, ks=_st(-128, 0, 128)) == ALIGN
     # fp32 strides need a multiple of 4 elements, bf16 a multiple of 8
     assert _chunk(lib, in_dt=BF16, qs=_st(0, 0, 132)) == ALIGN
+    # one head's K/V rows must span < 2 GiB on the bf16 path (32-bit buffer offsets)
+    assert _chunk(lib, ks=_st(0, 0, 2**27)) == UNSUP
+    assert _chunk(lib, vs=_st(0, 0, 2**24), Skv=2**7) == UNSUP
+    # the limit covers the loads of the three tiles the kernel fetches past the last one
+    assert _chunk(lib, ks=_st(0, 0, 2**22), Skv=128) == UNSUP  # (128 + 256) * 2^23 >= 2^31
     # empty problems are no-ops, even with NULL pointers
     assert _chunk(lib, q=None, k=None, v=None, o=None, lse=None, Sq=0) == OK
     assert _chunk(lib, q=None, k=None, v=None, o=None, lse=None, B=0) == OK

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from synth import workloads
-from parity_util import assert_parity, errors, to_device, to_f64
+from parity_util import BF16_MAX_ABS, BF16_MEAN_ABS, assert_parity, errors, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -126,13 +126,25 @@ def test_ulysses_share(ulysses):
 PLANS = ["chunks1", "chunks2", "chunks4", "chunks8", "ragged", "ring8"]
 
 
-def _all_rows_close(o, l, o1, l1, what):
-    """Every row of two fp32 results: max-abs <= 2e-2 and mean-abs <= 2e-3 for O and for LSE."""
+def _all_rows_close(o, l, o1, l1, what, host, scale, n_worst=4):
+    """Two fp32 results of the same problem, compared on every row.
+
+    Each result is within the bf16 gate of the oracle (max-abs 2e-2, mean-abs 2e-3) on the
+    sampled rows, so on any row two of them can differ by up to twice the gate; that is the
+    all-rows bound.  The rows where they differ most are then checked one by one against the
+    oracle, each result to the gate itself.
+    """
     do = (o.double() - o1.double()).abs()
     dl = (l.double() - l1.double()).abs()
     r = (do.max().item(), do.mean().item(), dl.max().item(), dl.mean().item())
-    print("  %s all rows vs chunks1: O max/mean %.3g/%.3g LSE max/mean %.3g/%.3g" % ((what,) + r), flush=True)
-    assert r[0] <= 2e-2 and r[1] <= 2e-3 and r[2] <= 2e-2 and r[3] <= 2e-3, r
+    print("  %s all rows vs reference run: O max/mean %.3g/%.3g LSE max/mean %.3g/%.3g" % ((what,) + r), flush=True)
+    assert r[0] <= 2 * BF16_MAX_ABS and r[1] <= 2 * BF16_MEAN_ABS, r
+    assert r[2] <= 2 * BF16_MAX_ABS and r[3] <= 2 * BF16_MEAN_ABS, r
+    per_row = do.amax(dim=(0, 1, 3))  # worst disagreement of each sequence row over heads
+    rows = sorted(torch.topk(per_row, min(n_worst, per_row.numel())).indices.tolist())
+    o_ref, l_ref = oracle.attention(host["q"], host["k"], host["v"], scale, q_rows=rows)
+    assert_parity(o[:, :, rows], l[:, :, rows], o_ref, l_ref, what="  %s, rows %s" % (what, rows))
+    assert_parity(o1[:, :, rows], l1[:, :, rows], o_ref, l_ref, what="  reference run, rows %s" % rows)
 
 
 def _bf16_is_rounded_f32(o_bf16, o_f32, l_bf16run, l_f32run):
@@ -152,7 +164,7 @@ def test_full_sequence_plans_agree(full_seq):
             full_seq.check(o, l, "full %s %s" % (name, mode))
             of, lf = full_seq.run(name, mode, out_dtype=torch.float32)
             _bf16_is_rounded_f32(o, of, l, lf)
-            _all_rows_close(of, lf, o1f, l1f, "%s %s" % (name, mode))
+            _all_rows_close(of, lf, o1f, l1f, "%s %s" % (name, mode), full_seq.host, full_seq.w.scale)
             del o, l, of, lf
 
 
@@ -166,4 +178,5 @@ def test_ring_share_equals_full_sequence_rows(ring_share):
     o, l = A().shard_fwd(qd, ring_share.dev["k"], ring_share.dev["v"], (44160,), out_dtype=torch.float32)
     o_r, l_r = ring_share.run(out_dtype=torch.float32)
     torch.cuda.synchronize()
-    _all_rows_close(o_r, l_r, o[:, :, :5520], l[:, :, :5520], "ring share vs full rows")
+    _all_rows_close(o_r, l_r, o[:, :, :5520], l[:, :, :5520], "ring share vs full rows", ring_share.host,
+                    ring_share.w.scale)
