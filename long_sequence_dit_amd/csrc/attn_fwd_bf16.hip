@@ -130,6 +130,9 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// bf16 pair {1, 1}
+__device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+
 // Buffer resource of a K or V head: base, no stride, num_records bytes; reads past the
 // end return zeros.
 struct Rsrc {
@@ -152,18 +155,18 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
 // loop.  Here the kernel orders these writes itself (an explicit vmcnt wait, then a
 // barrier, before any wave reads the buffer).  The loads have no register results, so
 // nothing the compiler allocates is written while they are in flight.  M0 holds the LDS
-// address; one wait state separates its write from the load that uses it.
+// address (an operand of the statement, so the compiler sets it and knows it is used);
+// one wait state separates its write from the load.
 template <int NB>
 __device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB], int soff) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
         asm volatile(
-            "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %1, %2, %3 offen lds"
+            "buffer_load_dwordx4 %0, %1, %2 offen lds"
             :
-            : "s"(dst + i * 1024u), "v"(goff[i]), "s"(rs.w), "s"(soff)
-            : "memory", "m0");
+            : "v"(goff[i]), "s"(rs.w), "s"(soff), "{m0}"(dst + i * 1024u)
+            : "memory");
 }
 
 // Per-wave state of the key loop.
@@ -220,7 +223,8 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
         } else if constexpr (POS == a + 2) {
             unsigned word = pack_bf16(sm.e[J][0], sm.e[J][1]);
             float& rs = (J & 1) ? sm.rs1 : sm.rs0;
-            rs += sm.e[J][0] + sm.e[J][1];
+            // the row sum adds the rounded probabilities that P.V uses: one dot2 per pair
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, word), kOnes, rs, false);
             asm volatile("" : "+v"(word), "+v"(rs));
             p[J >> 2][J & 3] = word;
         }
@@ -240,18 +244,20 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
     } else if constexpr (POS == 2) {
         sm.mt[8] = max3(sel_f(s, 24), sel_f(s, 25), sel_f(s, 26));
         sm.mt[9] = max3(sel_f(s, 27), sel_f(s, 28), sel_f(s, 29));
-        sm.mt[10] = fmaxf(sel_f(s, 30), sel_f(s, 31));
-        sm.mt[0] = max3(sm.mt[0], sm.mt[1], sm.mt[2]);
-        sm.mt[1] = max3(sm.mt[3], sm.mt[4], sm.mt[5]);
+        // every raw score enters through a three-input max (a two-input max of raw MFMA
+        // results would first quiet each input, one more instruction apiece)
+        sm.mt[10] = max3(sel_f(s, 30), sel_f(s, 31), sm.mt[0]);
+        sm.mt[1] = max3(sm.mt[1], sm.mt[2], sm.mt[3]);
     } else if constexpr (POS == 3) {
-        const float mx = max3(max3(sm.mt[0], sm.mt[1], sm.mt[6]), max3(sm.mt[7], sm.mt[8], sm.mt[9]), sm.mt[10]);
+        const float mx = max3(max3(sm.mt[1], sm.mt[4], sm.mt[5]), max3(sm.mt[6], sm.mt[7], sm.mt[8]),
+                              fmaxf(sm.mt[9], sm.mt[10]));
         half_pair(mx, sm.m0, sm.m1);
     } else if constexpr (POS == 4) {
         // Lazy rescale: a row's reference max only moves when the row's max exceeds it by
         // more than kRescale (log2 units).  Weights are then at most 2^kRescale, harmless in
         // fp32 and bf16, and O and l stay consistent because both use the same reference.
         // Lanes l and l+32 hold the same row and take the same decision.
-        const float m_tile = fmaxf(sm.m0, sm.m1) * w.c;
+        const float m_tile = __builtin_amdgcn_fmed3f(sm.m0, sm.m1, INFINITY) * w.c;  // max(m0, m1)
         sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
