@@ -85,7 +85,7 @@ typedef void* attn_stream_t;
 /* Merge modes of attn_shard_fwd (exactly one). */
 #define ATTN_MERGE_NWAY 1u   /* every chunk writes an fp32 partial; one n-way merge at the end */
 #define ATTN_MERGE_ONLINE 2u /* ring style: after each chunk, a pairwise merge into a running fp32 result */
-#define ATTN_MERGE_FUSED 4u  /* each chunk kernel merges its result into the running fp32 result in its epilogue */
+#define ATTN_MERGE_FUSED 4u  /* one kernel walks all chunks in order, the online-softmax state in registers */
 
 /*
  * attn_chunk_fwd — attention of every query row against ONE chunk of keys.
@@ -125,7 +125,9 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
 
 /*
  * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd needs
- * for this shape, chunk count and merge mode (0 when n_chunks == 1).
+ * for this shape, chunk count and merge mode: n fp32 partials (O and LSE) for
+ * ATTN_MERGE_NWAY, two for ATTN_MERGE_ONLINE, none for ATTN_MERGE_FUSED or
+ * when n_chunks == 1.
  * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
  */
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
@@ -143,7 +145,12 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *   order      HOST permutation of 0..n_chunks-1 giving the processing order,
  *              or NULL for 0, 1, ..., n_chunks-1
  *   flags      one of ATTN_MERGE_NWAY, ATTN_MERGE_ONLINE, ATTN_MERGE_FUSED
- *              (ignored when n_chunks == 1)
+ *              (ignored when n_chunks == 1).  FUSED is the ring's loop without
+ *              partials: one kernel folds chunk after chunk into its running
+ *              max, sum and output.  ONLINE and NWAY run one kernel per chunk
+ *              and merge the fp32 partials with attn_lse_merge's kernel, after
+ *              every chunk (as a ring receiving one block per step does) or
+ *              once at the end.
  *   workspace  DEVICE buffer of ws_bytes >= attn_shard_workspace_size(...),
  *              16-byte aligned (may be NULL when that size is 0)
  *   o, lse     as in attn_chunk_fwd, for the whole key sequence

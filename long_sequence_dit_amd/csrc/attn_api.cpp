@@ -4,11 +4,13 @@
 // The chunk loop is the per-rank work of Ring Attention and AllGather-KV
 // context parallelism (NVIDIA Technical Blog "Scaling AI Inference Across
 // Multiple GPUs Using NVIDIA TensorRT with Multi-Device Inference Support",
-// sections "Ring Attention" and "AllGather KV"): each chunk of keys yields a
-// partial output and LSE, and the partials are folded together by their
-// log-sum-exp weights.  Three merge schedules are offered: n-way at the end,
-// ring-style pairwise after every chunk, or fused into each chunk kernel's
-// epilogue.  All of them give attention over the whole key sequence.
+// sections "Ring Attention" and "AllGather KV"): the chunks of keys are folded
+// into the output one after another by an online softmax.  Three schedules are
+// offered: one kernel that walks every chunk in order with the softmax state in
+// registers (fused), or one kernel per chunk with the partial outputs merged by
+// their log-sum-exp weights, either pairwise after every chunk as a ring does
+// (online) or all at the end (n-way).  All give attention over the whole key
+// sequence.
 #include "attn.h"
 
 #include <math.h>
@@ -69,18 +71,8 @@ attn_status_t check_common(const void* q, attn_strides_t qs, const void* k, attn
     return ATTN_OK;
 }
 
-hipError_t run_chunk(const FwdArgs& a, attn_dtype_t in_dt, hipStream_t st) {
-    if (a.Skv == 0) {
-        // no keys: O = 0, LSE = -inf, merged with the running result if there is one
-        if (a.prev_o == nullptr) return lsdit::launch_fill_empty(a.o, a.os, a.o_bf16, a.lse, a.B, a.H, a.Sq, a.D, st);
-        MergeArgs m{};
-        m.n = 1;
-        m.o_parts[0] = a.prev_o;
-        m.lse_parts[0] = a.prev_lse;
-        m.B = a.B; m.H = a.H; m.Sq = a.Sq; m.D = a.D;
-        m.o = a.o; m.os = a.os; m.o_bf16 = a.o_bf16; m.lse = a.lse;
-        return lsdit::launch_lse_merge(m, st);
-    }
+// One launch over a.n_chunks >= 1 non-empty chunks.
+hipError_t run_fwd(const FwdArgs& a, attn_dtype_t in_dt, hipStream_t st) {
     return in_dt == ATTN_BF16 ? lsdit::launch_fwd_bf16(a, st) : lsdit::launch_fwd_f32(a, st);
 }
 
@@ -93,7 +85,7 @@ int slots_for(uint32_t flags, int32_t n) {
     if (n <= 1) return 0;
     if (flags == ATTN_MERGE_NWAY) return n;
     if (flags == ATTN_MERGE_ONLINE) return 2;
-    if (flags == ATTN_MERGE_FUSED) return 1;
+    if (flags == ATTN_MERGE_FUSED) return 0;  // one kernel, no partials
     return -1;
 }
 
@@ -109,6 +101,11 @@ attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, at
     bool noop = false;
     attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, Skv, D, scale, o, os, o_dt, lse, &noop);
     if (st != ATTN_OK || noop) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if (Skv == 0)  // no keys: O = 0, LSE = -inf
+        return lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s) == hipSuccess
+                   ? ATTN_OK
+                   : ATTN_ERR_HIP;
     FwdArgs a{};
     a.q = q; a.k = k; a.v = v;
     a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
@@ -116,7 +113,10 @@ attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, at
     a.lse = lse;
     a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
     a.scale = scale;
-    return run_chunk(a, in_dt, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    a.n_chunks = 1;
+    a.chunk_row[0] = 0;
+    a.chunk_len[0] = Skv;
+    return run_fwd(a, in_dt, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
@@ -175,6 +175,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
         ord[t] = c;
     }
     if (n_chunks > 1 && slots_for(flags, n_chunks) < 0) return ATTN_ERR_UNSUPPORTED;
+    static_assert(ATTN_MAX_CHUNKS <= lsdit::kMaxChunks, "chunk table too small");
 
     bool noop = false;
     attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, (int32_t)total, D, scale, o, os, o_dt,
@@ -194,15 +195,15 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     }
 
     const hipStream_t s = (hipStream_t)stream;
-    const size_t ie = esize(in_dt);
     FwdArgs base{};
-    base.q = q; base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
-    base.B = B; base.H = H; base.Sq = Sq; base.D = D; base.scale = scale;
-    auto chunk_args = [&](int c) {
+    base.q = q; base.k = k; base.v = v;
+    base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
+    base.B = B; base.H = H; base.Sq = Sq; base.Skv = (int32_t)total; base.D = D; base.scale = scale;
+    auto chunk_args = [&](int c) {  // one chunk, by its rows in the k and v tensors
         FwdArgs a = base;
-        a.k = (const char*)k + off[c] * ks.s * (int64_t)ie;
-        a.v = (const char*)v + off[c] * vs.s * (int64_t)ie;
-        a.Skv = chunk_len[c];
+        a.n_chunks = 1;
+        a.chunk_row[0] = (int32_t)off[c];
+        a.chunk_len[0] = chunk_len[c];
         return a;
     };
     auto to_final = [&](FwdArgs& a) {
@@ -218,28 +219,16 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
         return ok(lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s)) ? ATTN_OK
                                                                                                 : ATTN_ERR_HIP;
     }
-    if (n_live == 1) {
-        FwdArgs a = chunk_args(live[0]);
-        to_final(a);
-        return ok(run_chunk(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
-    }
-
-    if (flags == ATTN_MERGE_FUSED) {
+    if (n_live == 1 || flags == ATTN_MERGE_FUSED) {
+        // one kernel walks the chunks in processing order, the online-softmax state in registers
+        FwdArgs a = base;
+        a.n_chunks = n_live;
         for (int t = 0; t < n_live; ++t) {
-            FwdArgs a = chunk_args(live[t]);
-            if (t > 0) {
-                a.prev_o = slot_o(0);
-                a.ps = cs;
-                a.prev_lse = slot_lse(0);
-            }
-            if (t == n_live - 1) {
-                to_final(a);
-            } else {
-                a.o = slot_o(0); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(0);
-            }
-            if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+            a.chunk_row[t] = (int32_t)off[live[t]];
+            a.chunk_len[t] = chunk_len[live[t]];
         }
-        return ATTN_OK;
+        to_final(a);
+        return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
     }
 
     MergeArgs m{};
@@ -249,7 +238,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
             FwdArgs a = chunk_args(live[t]);
             const int slot = t == 0 ? 0 : 1;
             a.o = slot_o(slot); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(slot);
-            if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+            if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
             if (t == 0) continue;
             m.n = 2;
             m.o_parts[0] = slot_o(0); m.lse_parts[0] = slot_lse(0);
@@ -268,7 +257,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     for (int t = 0; t < n_live; ++t) {
         FwdArgs a = chunk_args(live[t]);
         a.o = slot_o(t); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(t);
-        if (!ok(run_chunk(a, in_dt, s))) return ATTN_ERR_HIP;
+        if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
         m.o_parts[t] = slot_o(t);
         m.lse_parts[t] = slot_lse(t);
     }

@@ -46,6 +46,7 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <stddef.h>
 
 namespace lsdit {
 namespace {
@@ -63,7 +64,6 @@ typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 constexpr int kPrefetch = 4;      // MFMA operands read this many slots ahead
@@ -168,6 +168,32 @@ __device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int 
             : "v"(goff[i]), "s"(rs.w), "s"(soff), "{m0}"(dst + i * 1024u)
             : "memory");
 }
+
+// Position in the key-tile sequence of a chunk list: the tile that starts at key row `row`
+// of chunk c, whose rows end at `end`.  Wave-uniform (scalar registers).  Chunk c's start row
+// and length sit in lane c of two vector registers and are read with readlane, so walking
+// needs no memory access.  Past the last chunk the walk stays at row `past` (beyond the
+// tensor, where the buffer loads read zeros).
+template <int BK>
+struct TileWalk {
+    int c, row, end;
+
+    __device__ __forceinline__ void enter(int ci, int n_chunks, int v_row, int v_len, int past) {
+        c = ci;
+        if (ci < n_chunks) {
+            row = __builtin_amdgcn_readlane(v_row, ci);
+            end = row + __builtin_amdgcn_readlane(v_len, ci);
+        } else {
+            row = past;
+            end = past + BK;
+        }
+    }
+    __device__ __forceinline__ void next(int n_chunks, int v_row, int v_len, int past) {
+        row += BK;
+        if (row >= end) enter(c + 1, n_chunks, v_row, v_len, past);
+    }
+    __device__ __forceinline__ int valid() const { return end - row; }  // >= BK: a full tile
+};
 
 // Per-wave state of the key loop.
 template <int D>
@@ -373,8 +399,19 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     const unsigned short* qp = (const unsigned short*)a.q + b * a.qs.b + h * a.qs.h;
     const unsigned short* kp = (const unsigned short*)a.k + b * a.ks.b + h * a.ks.h;
     const unsigned short* vp = (const unsigned short*)a.v + b * a.vs.b + h * a.vs.h;
-    const int Skv = a.Skv;
-    const int nkt = (Skv + C::BK - 1) / C::BK;
+    const int Skv = a.Skv;  // key rows of the k and v tensors
+
+    // ---- the chunk list: lane c holds chunk c's first row and length (read through the
+    // kernel-argument pointer, so the argument array is not copied to registers first)
+    const int n_chunks = a.n_chunks;
+    const int* const arg_rows =
+        (const int*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(FwdArgs, chunk_row));
+    const int* const arg_lens =
+        (const int*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(FwdArgs, chunk_len));
+    const int v_row = lane < n_chunks ? arg_rows[lane] : 0;
+    const int v_len = lane < n_chunks ? arg_lens[lane] : 0;
+    int nkt = 0;  // tiles over all chunks
+    for (int ci = 0; ci < n_chunks; ++ci) nkt += (__builtin_amdgcn_readlane(v_len, ci) + C::BK - 1) / C::BK;
 
     Wave<D> w;
     w.c = c;
@@ -412,11 +449,21 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     // LDS byte offsets of the tile buffers (the dynamic LDS block starts at offset 0)
     auto kbuf = [&](int t) { return (t % C::NSTAGE) * C::TILE_BYTES; };
     auto vbuf = [&](int t) { return (C::NSTAGE + t % C::NSTAGE) * C::TILE_BYTES; };
-    auto load_k = [&](int t) {
-        lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(t) + wave * C::BLKS_PER_WAVE * 1024, k_goff, t * C::BK * k_rs);
+    // Two walks over the tile sequence, one per tensor: the next K tile to load (tile t + 3
+    // during iteration t) and the next V tile (tile t + 1, which is also the next tile to
+    // mask).  Tile g of the sequence goes into buffer g mod NSTAGE.
+    TileWalk<C::BK> wk, wv;
+    wk.enter(0, n_chunks, v_row, v_len, Skv);
+    wv = wk;
+    auto load_k = [&](int g) {
+        lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
+        wk.next(n_chunks, v_row, v_len, Skv);
     };
-    auto load_v = [&](int t) {
-        lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(t) + wave * C::BLKS_PER_WAVE * 1024, v_goff, t * C::BK * v_rs);
+    auto load_v = [&](int g) {  // returns the tile's number of valid keys
+        const int valid = wv.valid();
+        lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff, wv.row * v_rs);
+        wv.next(n_chunks, v_row, v_len, Skv);
+        return valid;
     };
 
     // ---- per-lane LDS read offsets (bytes, within a buffer).  Each swizzle XOR only touches
@@ -436,8 +483,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 
     // Key of accumulator element (kb, r) is kb*32 + 8(r>>2) + 4hi + (r&3); compare its
     // compile-time part against valid - 4hi, so no table of per-lane key indices is kept live.
-    auto mask = [&](f32x16_t(&s)[2], int t) {
-        const int valid = Skv - t * C::BK;
+    // Rows of a tile past its chunk's end (another chunk's keys, or zeros past the tensor)
+    // get P = 0.
+    auto mask = [&](f32x16_t(&s)[2], int valid) {
         if (valid < C::BK) {
             const int lim = valid - 4 * hi;
 #pragma unroll
@@ -455,8 +503,8 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     load_k(0);
     load_k(1);
     load_k(2);
-    load_v(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tiles are in
+    const int valid0 = load_v(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
     __syncthreads();
 
     f32x16_t sc[2];      // scores: of tile t while its softmax runs, then of tile t+1
@@ -474,7 +522,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     };
     // tile 0: scores, then its softmax on its own
     stream<D, false, true, false>(w, lds, vbuf(0), kbuf(0), pB, sc, pB, sm);  // S_0
-    mask(sc, 0);
+    mask(sc, valid0);
     softmax_all<D>(w, sm, sc, pA);  // P_0 -> pA
     finish_softmax();
     __syncthreads();  // every wave is done with K buffer 0 before tile 3 overwrites it
@@ -488,14 +536,14 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     constexpr int kWaitPrev = 0x0F70 | (2 * C::BLKS_PER_WAVE);  // vmcnt(loads issued this iteration)
     auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4]) {
         load_k(t + 3);
-        load_v(t + 1);
+        const int valid = load_v(t + 1);
         if (t == 0) {
             stream<D, false, true, false>(w, lds, vbuf(0), kbuf(1), p_prev, sc, p_cur, sm);
         } else {
             stream<D, true, true, true>(w, lds, vbuf(t - 1), kbuf(t + 1), p_prev, sc, p_cur, sm);
             finish_softmax();
         }
-        if (t + 1 < nkt) mask(sc, t + 1);
+        if (t + 1 < nkt) mask(sc, valid);
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
     };
@@ -515,25 +563,13 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     else
         stream<D, true, false, false>(w, lds, vbuf(nkt - 1), kbuf(0), pB, sc, pA, sm);
 
-    // ---- epilogue: normalise, LSE, optional merge into the running result, store
+    // ---- epilogue: normalise, LSE, store
     float l0, l1;
     half_pair(w.l_run, l0, l1);
     const float l_tot = l0 + l1;
     const float inv_l = 1.f / l_tot;
-    float lse2 = w.m_run + log2f(l_tot);  // log2 domain
-    float wa = 0.f, wb = inv_l;            // out = wa * prev + wb * acc
-    const int64_t lrow = (int64_t)bh * a.Sq + qrow;
-    if (a.prev_o != nullptr && qrow < a.Sq) {
-        const float lp = a.prev_lse[lrow] * kLog2e;
-        const float M = fmaxf(lp, lse2);
-        const float ea = fast_exp2(lp - M), eb = fast_exp2(lse2 - M);
-        const float tot = ea + eb;
-        wa = ea / tot;
-        wb = eb / tot * inv_l;
-        lse2 = M + log2f(tot);
-    }
+    const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
     if (qrow < a.Sq) {
-        const float* pp = a.prev_o ? a.prev_o + b * a.ps.b + h * a.ps.h + (int64_t)qrow * a.ps.s : nullptr;
         if (a.o_bf16) {
             unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
 #pragma unroll
@@ -541,17 +577,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int d = 32 * dt + 8 * r4 + 4 * hi;
-                    float x[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * wb;
-                    if (pp) {
-                        const f32x4_t pv = *(const f32x4_t*)(pp + d);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] += wa * pv[e];
-                    }
                     u32x2_t wd;
-                    wd[0] = pack_bf16(x[0], x[1]);
-                    wd[1] = pack_bf16(x[2], x[3]);
+                    wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
+                    wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
                     *(u32x2_t*)(op + d) = wd;
                 }
         } else {
@@ -563,18 +591,12 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                     const int d = 32 * dt + 8 * r4 + 4 * hi;
                     f32x4_t x;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * wb;
-                    if (pp) {
-                        const f32x4_t pv = *(const f32x4_t*)(pp + d);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] += wa * pv[e];
-                    }
+                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * inv_l;
                     *(f32x4_t*)(op + d) = x;
                 }
         }
+        if (hi == 0) a.lse[(int64_t)bh * a.Sq + qrow] = lse2 * kLn2;
     }
-    // prev_lse may alias lse: the store depends on the loaded value, so it cannot overtake it.
-    if (qrow < a.Sq && hi == 0) a.lse[lrow] = lse2 * kLn2;
 }
 
 template <int D>

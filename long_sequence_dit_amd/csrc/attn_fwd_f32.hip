@@ -14,13 +14,13 @@
 #include "kernels.h"
 
 #include <math.h>
+#include <stddef.h>
 
 namespace lsdit {
 namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kRows = 64;   // query rows per workgroup
 constexpr int kBK = 32;     // keys per tile
@@ -50,12 +50,18 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int k0 = 0; k0 < a.Skv; k0 += kBK) {
-        const int n = a.Skv - k0 < kBK ? a.Skv - k0 : kBK;
+    // the chunk list, in processing order (read through the kernel-argument pointer)
+    const int* const arg_rows =
+        (const int*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(FwdArgs, chunk_row));
+    const int* const arg_lens =
+        (const int*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(FwdArgs, chunk_len));
+    for (int ci = 0; ci < a.n_chunks; ++ci)
+    for (int row0 = arg_rows[ci], len = arg_lens[ci], k0 = 0; k0 < len; k0 += kBK) {
+        const int n = len - k0 < kBK ? len - k0 : kBK;
         __syncthreads();
         for (int idx = tid; idx < kBK * (D / 4); idx += kThreads) {
             const int r = idx / (D / 4), c4 = idx % (D / 4);
-            const int key = k0 + (r < n ? r : n - 1);
+            const int key = row0 + k0 + (r < n ? r : n - 1);
             *(f32x4_t*)&Ks[r][4 * c4] = *(const f32x4_t*)(kp + (int64_t)key * a.ks.s + 4 * c4);
             *(f32x4_t*)&Vs[r][4 * c4] = *(const f32x4_t*)(vp + (int64_t)key * a.vs.s + 4 * c4);
         }
@@ -93,25 +99,11 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
     }
 
     if (qrow >= a.Sq) return;
-    float lse2 = m_run + log2f(l_run);
-    float wa = 0.f, wb = 1.f / l_run;
-    const int64_t lrow = (int64_t)bh * a.Sq + qrow;
-    const float* pp = nullptr;
-    if (a.prev_o != nullptr) {
-        pp = a.prev_o + b * a.ps.b + h * a.ps.h + (int64_t)qrow * a.ps.s + part * DQ;
-        const float lp = a.prev_lse[lrow] * kLog2e;
-        const float M = fmaxf(lp, lse2);
-        const float ea = exp2f(lp - M), eb = exp2f(lse2 - M);
-        const float tot = ea + eb;
-        wa = ea / tot;
-        wb = eb / tot / l_run;
-        lse2 = M + log2f(tot);
-    }
+    const float inv_l = 1.f / l_run;
     float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s + part * DQ;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) op[d] = o[d] * wb + (pp ? wa * pp[d] : 0.f);
-    // every lane of the row has read prev_lse above (the stores depend on it)
-    if (part == 0) a.lse[lrow] = lse2 * kLn2;
+    for (int d = 0; d < DQ; ++d) op[d] = o[d] * inv_l;
+    if (part == 0) a.lse[(int64_t)bh * a.Sq + qrow] = (m_run + log2f(l_run)) * kLn2;
 }
 
 template <int D>

@@ -12,7 +12,8 @@ struct Strides {
     int64_t b, h, s;
 };
 
-// One chunk-attention launch.  Pointers are device pointers.
+// One attention launch over a list of key chunks.  Pointers are device pointers.
+constexpr int kMaxChunks = 64;
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -22,11 +23,14 @@ struct FwdArgs {
     Strides os;
     int o_bf16;
     float* lse;          // [B, H, Sq] fp32 contiguous
-    const float* prev_o; // optional running fp32 result merged in the epilogue (may alias o)
-    Strides ps;
-    const float* prev_lse;  // [B, H, Sq] (may alias lse); NULL when prev_o is NULL
-    int B, H, Sq, Skv, D;
+    int B, H, Sq, Skv, D;  // Skv: key rows of the k and v tensors
     float scale;
+    // The keys attended, chunk by chunk in processing order: chunk c is rows
+    // [chunk_row[c], chunk_row[c] + chunk_len[c]) of k and v.  One launch folds every chunk
+    // into one online softmax, so the result is attention over the union of the chunks.
+    int n_chunks;        // 1 .. kMaxChunks
+    int chunk_row[kMaxChunks];
+    int chunk_len[kMaxChunks];  // each > 0
 };
 
 // Merge of up to kMaxMergeParts fp32 partials (contiguous [B,H,Sq,D] / [B,H,Sq]).

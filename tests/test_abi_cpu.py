@@ -134,10 +134,11 @@ def test_shard_fwd_argument_errors(attn):
     assert _shard(lib, order=(1, -1)) == SHAPE
     assert _shard(lib, flags=0) == UNSUP
     assert _shard(lib, flags=3) == UNSUP
-    assert _shard(lib, ws=None) == WS
-    need = lib.attn_shard_workspace_size(1, 2, 10, 128, 2, 4)
-    assert _shard(lib, ws_bytes=need - 1) == WS
-    assert _shard(lib, ws=P + 8, ws_bytes=need) == ALIGN
+    for flags in (1, 2):  # n-way and online keep fp32 partials in the workspace
+        assert _shard(lib, ws=None, flags=flags) == WS
+        need = lib.attn_shard_workspace_size(1, 2, 10, 128, 2, flags)
+        assert _shard(lib, ws_bytes=need - 1, flags=flags) == WS
+        assert _shard(lib, ws=P + 8, ws_bytes=need, flags=flags) == ALIGN
     assert _shard(lib, D=80) == UNSUP
     assert _shard(lib, q=None) == NULL
     assert _shard(lib, in_dt=F32, o_dt=BF16) == DTYPE
@@ -150,7 +151,7 @@ def test_workspace_sizes(attn):
     slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot   # n-way
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 2 * slot   # online
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == slot       # fused
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == 0          # fused: no partials
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0

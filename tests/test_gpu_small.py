@@ -104,6 +104,23 @@ def test_shard_modes_orders_and_empty_chunks(mode):
         assert_parity(o, l, o_ref, l_ref, what="shard %s order %s" % (mode, order))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("mode", ["fused", "nway"])
+def test_max_chunks_random_lengths_and_order(dtype, mode):
+    """64 chunks (the most one call takes): random lengths from 0 to 150 (tiles that end
+    mid-chunk, chunks shorter than a tile, empty chunks) walked in a random order."""
+    rng = np.random.default_rng(11)
+    lens = tuple(int(x) for x in rng.integers(0, 151, size=64))
+    order = tuple(int(x) for x in rng.permutation(64))
+    B, H, Sq, D = 1, 2, 130, 64
+    kind = synth.KIND_BF16 if dtype == "bf16" else synth.KIND_F32
+    q, k, v = _inputs(B, H, Sq, sum(lens), D, kind=kind, seed=9)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
+    o, l = A().shard_fwd(to_device(q), to_device(k), to_device(v), lens, order, mode=mode)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, fp32=dtype == "fp32", what="64 chunks %s %s" % (dtype, mode))
+
+
 def test_bf16_chunk_partials_and_merge():
     B, H, Sq, D = 1, 2, 200, 128
     lens = (70, 130, 64)
