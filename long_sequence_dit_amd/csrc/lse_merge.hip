@@ -10,8 +10,11 @@
 // The merge streams n fp32 partials and writes one output: it is bound by
 // HBM bandwidth.  Each lane owns 4 consecutive elements of a row (16-byte
 // loads), a row's D/4 lanes sit in one wave, and every part is read exactly
-// once.  Parts whose LSE is -inf carry no weight; if all are -inf the output
-// is O = 0, LSE = -inf.
+// once.  Parts are taken in batches (2 to 16 parts, the smallest that covers
+// n, up to 16) with all of a batch's loads issued before any is used, so each
+// lane keeps a batch of loads in flight.
+// Parts whose LSE is -inf carry no weight; if all are -inf the output is
+// O = 0, LSE = -inf.
 #include "kernels.h"
 
 #include <math.h>
@@ -46,6 +49,7 @@ __device__ __forceinline__ void store4(void* o, Strides os, int o_bf16, int H, i
     }
 }
 
+template <int kBatch>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int lanes_per_row = a.D / 4;
     const int rows_per_block = kThreads / lanes_per_row;
@@ -53,20 +57,41 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int64_t row = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / lanes_per_row;
     const int d = 4 * (threadIdx.x % lanes_per_row);
     if (row >= rows) return;
+    const int n = a.n;
 
-    // natural-log domain, so that a single part with weight exp(0) = 1 passes through exactly
-    float M = -INFINITY;
-    for (int c = 0; c < a.n; ++c) M = fmaxf(M, a.lse_parts[c][row]);
+    // LSE of the union, natural-log domain (so that a single live part gets weight
+    // exp(0) = 1 and passes through exactly): running max M and sum of exp(LSE_c - M)
+    float M = -INFINITY, tot = 0.f;
+    for (int c0 = 0; c0 < n; c0 += kBatch) {
+        float l[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) l[u] = c0 + u < n ? a.lse_parts[c0 + u][row] : -INFINITY;
+        float mb = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, l[u]);
+        if (mb == -INFINITY) continue;  // nothing live in this batch
+        const float m_new = fmaxf(M, mb);
+        float sb = 0.f;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) sb += expf(l[u] - m_new);
+        tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + sb;
+        M = m_new;
+    }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lse_out = -INFINITY;
     if (M != -INFINITY) {
-        float tot = 0.f;
-        for (int c = 0; c < a.n; ++c) tot += expf(a.lse_parts[c][row] - M);
         const float L = M + logf(tot);
-        for (int c = 0; c < a.n; ++c) {
-            const float w = expf(a.lse_parts[c][row] - L);
-            const f32x4_t x = *(const f32x4_t*)(a.o_parts[c] + row * a.D + d);
-            acc += w * x;
+        for (int c0 = 0; c0 < n; c0 += kBatch) {
+            f32x4_t x[kBatch];
+            float w[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const bool live = c0 + u < n;
+                x[u] = live ? *(const f32x4_t*)(a.o_parts[c0 + u] + row * a.D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                w[u] = live ? a.lse_parts[c0 + u][row] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) acc += expf(w[u] - L) * x[u];
         }
         lse_out = L;
     }
@@ -94,7 +119,15 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (a.n <= 2)
+        hipLaunchKernelGGL(merge_kernel<2>, grid, block, 0, stream, a);
+    else if (a.n <= 4)
+        hipLaunchKernelGGL(merge_kernel<4>, grid, block, 0, stream, a);
+    else if (a.n <= 8)
+        hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(merge_kernel<16>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
