@@ -202,7 +202,7 @@ struct Wave {
     bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
     float m_run;           // reference max (scaled, log2 domain)
     float l_run;           // this lane's share of the running row sum
-    int k_base, v_base;    // per-lane LDS read offsets (see the kernel)
+    unsigned k_base, v_base;  // per-lane LDS read addresses in buffer 0 (see the kernel)
     float c;               // scale * log2(e)
 };
 
@@ -307,24 +307,26 @@ __device__ __forceinline__ void softmax_all(Wave<D>& w, Soft& sm, const f32x16_t
 // are untouched); XOR-ing the slot constant into that loop-variant value keeps the compiler
 // from hoisting a table of loop-invariant addresses out of the key loop (and spilling it).
 template <int D, int SLOT>
-__device__ __forceinline__ u32x4_t read_opnd(const lds_u8_t* lds, int vb, int kb_) {
+__device__ __forceinline__ u32x4_t read_opnd(unsigned vb, unsigned kb_) {
     using C = Cfg<D>;
+    // vb and kb_ are LDS byte addresses, so each read's address is one XOR of a per-lane
+    // register with a constant, plus the instruction offset
     if constexpr (SLOT < C::N_PV) {
         constexpr int ks = SLOT / (D / 32), dt = SLOT % (D / 32);
-        const lds_u8_t* base = lds + (vb ^ (dt << 6)) + 16 * ks * C::ROW_BYTES;
-        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)base));
-        const u32x2_t hi =
-            __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + 8 * C::ROW_BYTES)));
+        const unsigned a = (vb ^ (dt << 6)) + 16 * ks * C::ROW_BYTES;
+        const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)a));
+        const u32x2_t hi = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)(a + 8 * C::ROW_BYTES)));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     } else {
         constexpr int sl = SLOT - C::N_PV, kk = sl >> 1, kb = sl & 1;
-        return *(const lds_u32x4_t*)(lds + (kb_ ^ (kk << 5)) + kb * 32 * C::ROW_BYTES);
+        return *(const lds_u32x4_t*)(size_t)((kb_ ^ (kk << 5)) + kb * 32 * C::ROW_BYTES);
     }
 }
 
 // Slot SLOT of a stream (see stream()), then the following slots.
 template <int D, bool DO_PV, bool DO_S, bool DO_SM, int SLOT>
-__device__ __forceinline__ void stream_slots(Wave<D>& w, const lds_u8_t* lds, int vb, int kb_, u32x4_t (&ring)[kPrefetch],
+__device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch],
                                              const u32x4_t (&p_prev)[4], f32x16_t (&s)[2], u32x4_t (&p_cur)[4],
                                              Soft& sm) {
     using C = Cfg<D>;
@@ -349,20 +351,20 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, const lds_u8_t* lds, in
                                                                 0, 0);
             }
         }
-        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(lds, vb, kb_);
+        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(vb, kb_);
         if constexpr (DO_SM && pos < C::N_PV + 2) softmax_slot<D, pos>(w, sm, s, p_cur);
         __builtin_amdgcn_sched_barrier(0);
-        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, lds, vb, kb_, ring, p_prev, s, p_cur, sm);
+        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, vb, kb_, ring, p_prev, s, p_cur, sm);
     }
 }
 
 template <int D, bool DO_PV, int I = 0>
-__device__ __forceinline__ void ring_fill(const lds_u8_t* lds, int vb, int kb_, u32x4_t (&ring)[kPrefetch], int last) {
+__device__ __forceinline__ void ring_fill(unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch], int last) {
     using C = Cfg<D>;
     constexpr int first = DO_PV ? 0 : C::N_PV;
     if constexpr (I < kPrefetch) {
-        if (first + I < last) ring[I] = read_opnd<D, first + I>(lds, vb, kb_);
-        ring_fill<D, DO_PV, I + 1>(lds, vb, kb_, ring, last);
+        if (first + I < last) ring[I] = read_opnd<D, first + I>(vb, kb_);
+        ring_fill<D, DO_PV, I + 1>(vb, kb_, ring, last);
     }
 }
 
@@ -370,18 +372,18 @@ __device__ __forceinline__ void ring_fill(const lds_u8_t* lds, int vb, int kb_, 
 // softmax of the scores in s into p_cur (if DO_SM; on the P.V slots), then the scores of the
 // tile at k0 into s (if DO_S; on the later slots, after the softmax has read s).
 template <int D, bool DO_PV, bool DO_S, bool DO_SM>
-__device__ __forceinline__ void stream(Wave<D>& w, const lds_u8_t* lds, int v0, int k0, const u32x4_t (&p_prev)[4],
+__device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, const u32x4_t (&p_prev)[4],
                                        f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
     using C = Cfg<D>;
     static_assert(!DO_SM || (DO_PV && DO_S), "the softmax needs the full stream's slots");
     static_assert(C::N_PV >= 8 && C::N_S >= 2, "stream too short for the softmax pipeline");
     constexpr int first = DO_PV ? 0 : C::N_PV;
     constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
-    const int vb = w.v_base | v0, kb_ = w.k_base | k0;
+    const unsigned vb = w.v_base | v0, kb_ = w.k_base | k0;
     u32x4_t ring[kPrefetch];
-    ring_fill<D, DO_PV>(lds, vb, kb_, ring, last);
+    ring_fill<D, DO_PV>(vb, kb_, ring, last);
     __builtin_amdgcn_sched_barrier(0);
-    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, lds, vb, kb_, ring, p_prev, s, p_cur, sm);
+    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, vb, kb_, ring, p_prev, s, p_cur, sm);
 }
 
 template <int D>
@@ -444,31 +446,40 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         k_goff[i] = row * k_rs + (slot ^ k_swz<D>(row)) * 16;
         v_goff[i] = row * v_rs + (slot ^ v_swz<D>(row)) * 16;
     }
-    lds_u8_t* const lds = (lds_u8_t*)smem;
-    const unsigned lds_base = (unsigned)(size_t)lds;  // LDS byte address of the tile block
+    // The kernel declares no static LDS, so its dynamic block (smem) starts at LDS address 0
+    // and every LDS access below is a plain byte address; a CPU test checks that the built
+    // kernel has no static LDS.  (Pointer arithmetic on smem instead costs one add per
+    // address: the block's address is a link-time constant the compiler cannot fold.)
+    (void)smem;
+    constexpr unsigned lds_base = 0;
     // LDS byte offsets of the tile buffers (the dynamic LDS block starts at offset 0)
     auto kbuf = [&](int t) { return (t % C::NSTAGE) * C::TILE_BYTES; };
     auto vbuf = [&](int t) { return (C::NSTAGE + t % C::NSTAGE) * C::TILE_BYTES; };
-    // Two walks over the tile sequence, one per tensor: the next K tile to load (tile t + 3
-    // during iteration t) and the next V tile (tile t + 1, which is also the next tile to
-    // mask).  Tile g of the sequence goes into buffer g mod NSTAGE.
-    TileWalk<C::BK> wk, wv;
+    // Three walks over the tile sequence: the next K tile to load (tile t + NSTAGE during
+    // iteration t), the next V tile to load (tile t + NSTAGE - 2) and the next tile to mask
+    // (tile t + 1).  Tile g of the sequence goes into buffer g mod NSTAGE.
+    TileWalk<C::BK> wk, wv, wm;
     wk.enter(0, n_chunks, v_row, v_len, Skv);
     wv = wk;
+    wm = wk;
     auto load_k = [&](int g) {
         lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
         wk.next(n_chunks, v_row, v_len, Skv);
     };
-    auto load_v = [&](int g) {  // returns the tile's number of valid keys
-        const int valid = wv.valid();
+    auto load_v = [&](int g) {
         lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff, wv.row * v_rs);
         wv.next(n_chunks, v_row, v_len, Skv);
+    };
+    auto next_valid = [&]() {  // valid keys of the next tile to mask
+        const int valid = wm.valid();
+        wm.next(n_chunks, v_row, v_len, Skv);
         return valid;
     };
 
-    // ---- per-lane LDS read offsets (bytes, within a buffer).  Each swizzle XOR only touches
-    // chunk-index bits that the loop index sets independently, so one per-lane base XOR-ed
-    // with a compile-time constant addresses every operand; row steps are additive.
+    // ---- per-lane LDS read addresses in buffer 0 (bytes; a buffer ORs in a multiple of
+    // 16 KiB).  Each swizzle XOR only touches chunk-index bits that the loop index sets
+    // independently, so one per-lane address XOR-ed with a compile-time constant addresses
+    // every operand; row steps are additive.
     // K operand (kb, kk): row kb*32 + (lane&31), chunk 2kk + hi  ->  k_base ^ (kk << 5)
     // (k_swz(row + 32) == k_swz(row)).
     w.k_base = (lane & 31) * C::ROW_BYTES + ((hi ^ k_swz<D>(lane & 31)) * 16);
@@ -498,12 +509,13 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 
     // ---- prologue.  Zero the tiles first: key rows past the end of a chunk are masked
     // (P = 0), and zeros there keep 0 * V finite whatever the loads leave in those rows.
-    for (int i = tid; i < C::LDS_BYTES / 16; i += C::NT) ((lds_u32x4_t*)lds)[i] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = tid; i < C::LDS_BYTES / 16; i += C::NT)
+        *(lds_u32x4_t*)(size_t)(lds_base + 16u * i) = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
-    load_k(0);
-    load_k(1);
-    load_k(2);
-    const int valid0 = load_v(0);
+#pragma unroll
+    for (int g = 0; g < C::NSTAGE; ++g) load_k(g);
+#pragma unroll
+    for (int g = 0; g < C::NSTAGE - 2; ++g) load_v(g);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
     __syncthreads();
 
@@ -521,29 +533,32 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         }
     };
     // tile 0: scores, then its softmax on its own
-    stream<D, false, true, false>(w, lds, vbuf(0), kbuf(0), pB, sc, pB, sm);  // S_0
-    mask(sc, valid0);
+    stream<D, false, true, false>(w, vbuf(0), kbuf(0), pB, sc, pB, sm);  // S_0
+    mask(sc, next_valid());
     softmax_all<D>(w, sm, sc, pA);  // P_0 -> pA
     finish_softmax();
     __syncthreads();  // every wave is done with K buffer 0 before tile 3 overwrites it
 
-    // ---- key loop.  Iteration t: issue K_{t+3} (into K_t's buffer) and V_{t+1} (into
-    // V_{t-2}'s buffer); stream P.V of tile t-1 with the softmax of tile t, then the scores of
-    // tile t+1; then wait for the previous iteration's loads (K_{t+2}, V_t) and sync.  K_t is
-    // read in iteration t-1 (scores) and V_t in iteration t+1 (P.V), each before the barrier
-    // that precedes its buffer's refill.  Scores of tile nkt are computed from a stale buffer
-    // and never used.  The probability registers swap roles every iteration (pA <-> pB).
-    constexpr int kWaitPrev = 0x0F70 | (2 * C::BLKS_PER_WAVE);  // vmcnt(loads issued this iteration)
+    // ---- key loop.  Iteration t: issue K_{t+NSTAGE} (into K_t's buffer) and V_{t+NSTAGE-2}
+    // (into V_{t-2}'s buffer); stream P.V of tile t-1 with the softmax of tile t, then the
+    // scores of tile t+1; then wait for the loads that iteration t+1 reads (K_{t+2}, V_t, both
+    // issued NSTAGE - 2 iterations ago) and sync.  K_t is read in iteration t-1 (scores) and
+    // V_t in iteration t+1 (P.V), each before the barrier that precedes its buffer's refill.
+    // Scores of tile nkt are computed from a stale buffer and never used.  The probability
+    // registers swap roles every iteration (pA <-> pB).
+    // vmcnt(loads issued in the last NSTAGE - 2 iterations)
+    constexpr int kWaitPrev = 0x0F70 | ((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE);
+    static_assert((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE < 16, "vmcnt field");
     auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4]) {
-        load_k(t + 3);
-        const int valid = load_v(t + 1);
+        load_k(t + C::NSTAGE);
+        load_v(t + C::NSTAGE - 2);
         if (t == 0) {
-            stream<D, false, true, false>(w, lds, vbuf(0), kbuf(1), p_prev, sc, p_cur, sm);
+            stream<D, false, true, false>(w, vbuf(0), kbuf(1), p_prev, sc, p_cur, sm);
         } else {
-            stream<D, true, true, true>(w, lds, vbuf(t - 1), kbuf(t + 1), p_prev, sc, p_cur, sm);
+            stream<D, true, true, true>(w, vbuf(t - 1), kbuf(t + 1), p_prev, sc, p_cur, sm);
             finish_softmax();
         }
-        if (t + 1 < nkt) mask(sc, valid);
+        if (t + 1 < nkt) mask(sc, next_valid());
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
     };
@@ -559,9 +574,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     }
     // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)
     if (nkt & 1)
-        stream<D, true, false, false>(w, lds, vbuf(nkt - 1), kbuf(0), pA, sc, pB, sm);
+        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pA, sc, pB, sm);
     else
-        stream<D, true, false, false>(w, lds, vbuf(nkt - 1), kbuf(0), pB, sc, pA, sm);
+        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pB, sc, pA, sm);
 
     // ---- epilogue: normalise, LSE, store
     float l0, l1;
