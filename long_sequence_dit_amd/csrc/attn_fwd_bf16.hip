@@ -26,17 +26,19 @@
 //    slots carry a fixed share of the softmax of tile t: the max tree, then
 //    the probabilities as a three-stage software pipeline (FMA, exp, pack
 //    and sum in consecutive slots), so no slot holds a dependent VALU chain
-//    that would stall the wave's next MFMA, and the scores of tile t are dead
-//    before those of tile t+1 are born.  Scheduling barriers pin this order:
-//    left to itself the compiler moves each LDS read next to its MFMA
-//    (exposing the LDS latency on every MFMA) and bunches the MFMAs apart
-//    from the VALU;
+//    that would stall the wave's next MFMA.  The scores of alternate tiles
+//    sit in two register buffers, so the softmax spreads over all the slots
+//    while the score MFMAs fill the other buffer.  Scheduling barriers pin
+//    this order: left to itself the compiler moves each LDS read next to its
+//    MFMA (exposing the LDS latency on every MFMA) and bunches the MFMAs
+//    apart from the VALU;
 //  * K/V tiles of 64 rows go HBM -> LDS directly (buffer loads with the LDS
 //    destination) into three buffers each, K issued two iterations and V
 //    one iteration before use, through buffer resources whose out-of-range
-//    rows read as zero (and are masked); LDS rows are XOR swizzled in
-//    16-byte chunks so both the row reads of K and the transposed reads of V
-//    are free of bank conflicts;
+//    rows read as zero (and are masked); waves 0-3 issue all of them (the
+//    older wave of each SIMD, which otherwise idles at the loop barrier);
+//    LDS rows are XOR swizzled in 16-byte chunks so both the row reads of K
+//    and the transposed reads of V are free of bank conflicts;
 //  * exponentials are base 2 with scale*log2(e) folded into one FMA; the
 //    running output is rescaled only when a row maximum grows by more than
 //    2^8.
@@ -67,6 +69,10 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 constexpr int kPrefetch = 4;      // MFMA operands read this many slots ahead
+// The softmax of a tile runs over every slot of the stream (its scores in a second register
+// buffer, so the score MFMAs of the next tile may overwrite the other one meanwhile), rather
+// than over the P.V slots only: half the VALU work next to each MFMA.
+constexpr bool kSpread = true;
 
 template <int D>
 struct Cfg {
@@ -81,7 +87,11 @@ struct Cfg {
     static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;
     static constexpr int ROWS_PER_BLK = 64 / CH;            // rows one wave-wide 1 KiB load covers
     static constexpr int BLKS = BK / ROWS_PER_BLK;          // 1 KiB blocks per tile
-    static constexpr int BLKS_PER_WAVE = BLKS / NW;
+    // Waves 0-3 (one per SIMD) issue all tile loads.  Each SIMD runs wave w and wave w+4,
+    // and the older one (w) wins issue arbitration and reaches the loop barrier first, so
+    // its idle time there absorbs the load issue that would otherwise delay wave w+4.
+    static constexpr int LOADERS = NW / 2;
+    static constexpr int BLKS_PER_WAVE = BLKS / LOADERS;
     static_assert(BLKS % NW == 0, "tile must split evenly over the waves");
     static constexpr int N_PV = (D / 32) * 4;               // P.V slots: (ks, dt), dt fastest
     static constexpr int N_S = (D / 16) * 2;                // score slots: (kk, kb), kb fastest
@@ -209,6 +219,14 @@ struct Wave {
 // Element f (0..31) of a lane's score tile (f is a compile-time constant after unrolling).
 __device__ __forceinline__ float sel_f(const f32x16_t (&s)[2], int f) { return s[f >> 4][f & 15]; }
 
+// Last slot of the softmax pipeline's first stage (see pair_slot): with kSpread the pipeline
+// ends on the stream's last slot; otherwise on the last P.V slot + 2, so that every score is
+// read before the score MFMAs overwrite it.
+template <int D>
+__host__ __device__ constexpr int last_a_slot() {
+    return kSpread ? Cfg<D>::N_PV + Cfg<D>::N_S - 3 : Cfg<D>::N_PV - 1;
+}
+
 // Softmax state carried across the slots of one stream.
 struct Soft {
     float mt[11];           // partial maxima
@@ -290,13 +308,13 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
         sm.rs0 = 0.f;
         sm.rs1 = 0.f;
     }
-    pair_stages<POS, Cfg<D>::N_PV - 1>(w.c, sm, s, p);
+    pair_stages<POS, last_a_slot<D>()>(w.c, sm, s, p);
 }
 
 // All softmax positions in order (for a tile whose softmax runs on its own).
 template <int D, int POS = 0>
 __device__ __forceinline__ void softmax_all(Wave<D>& w, Soft& sm, const f32x16_t (&s)[2], u32x4_t (&p)[4]) {
-    if constexpr (POS < Cfg<D>::N_PV + 2) {
+    if constexpr (POS < last_a_slot<D>() + 3) {
         softmax_slot<D, POS>(w, sm, s, p);
         softmax_all<D, POS + 1>(w, sm, s, p);
     }
@@ -327,8 +345,8 @@ __device__ __forceinline__ u32x4_t read_opnd(unsigned vb, unsigned kb_) {
 // Slot SLOT of a stream (see stream()), then the following slots.
 template <int D, bool DO_PV, bool DO_S, bool DO_SM, int SLOT>
 __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch],
-                                             const u32x4_t (&p_prev)[4], f32x16_t (&s)[2], u32x4_t (&p_cur)[4],
-                                             Soft& sm) {
+                                             const u32x4_t (&p_prev)[4], const f32x16_t (&s_cur)[2],
+                                             f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
     using C = Cfg<D>;
     constexpr int first = DO_PV ? 0 : C::N_PV;
     constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
@@ -352,9 +370,9 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned k
             }
         }
         if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(vb, kb_);
-        if constexpr (DO_SM && pos < C::N_PV + 2) softmax_slot<D, pos>(w, sm, s, p_cur);
+        if constexpr (DO_SM && pos < last_a_slot<D>() + 3) softmax_slot<D, pos>(w, sm, s_cur, p_cur);
         __builtin_amdgcn_sched_barrier(0);
-        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, vb, kb_, ring, p_prev, s, p_cur, sm);
+        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
     }
 }
 
@@ -373,7 +391,7 @@ __device__ __forceinline__ void ring_fill(unsigned vb, unsigned kb_, u32x4_t (&r
 // tile at k0 into s (if DO_S; on the later slots, after the softmax has read s).
 template <int D, bool DO_PV, bool DO_S, bool DO_SM>
 __device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, const u32x4_t (&p_prev)[4],
-                                       f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
+                                       const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
     using C = Cfg<D>;
     static_assert(!DO_SM || (DO_PV && DO_S), "the softmax needs the full stream's slots");
     static_assert(C::N_PV >= 8 && C::N_S >= 2, "stream too short for the softmax pipeline");
@@ -383,7 +401,7 @@ __device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, const u32x4_t
     u32x4_t ring[kPrefetch];
     ring_fill<D, DO_PV>(vb, kb_, ring, last);
     __builtin_amdgcn_sched_barrier(0);
-    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, vb, kb_, ring, p_prev, s, p_cur, sm);
+    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
 }
 
 template <int D>
@@ -463,11 +481,13 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     wv = wk;
     wm = wk;
     auto load_k = [&](int g) {
-        lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
+        if (wave < C::LOADERS)
+            lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
         wk.next(n_chunks, v_row, v_len, Skv);
     };
     auto load_v = [&](int g) {
-        lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff, wv.row * v_rs);
+        if (wave < C::LOADERS)
+            lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff, wv.row * v_rs);
         wv.next(n_chunks, v_row, v_len, Skv);
     };
     auto next_valid = [&]() {  // valid keys of the next tile to mask
@@ -519,8 +539,11 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
     __syncthreads();
 
-    f32x16_t sc[2];      // scores: of tile t while its softmax runs, then of tile t+1
-    u32x4_t pA[4], pB[4];  // probabilities of alternate tiles
+    // Scores of alternate tiles (one buffer without kSpread: the softmax of tile t then reads
+    // it before the score MFMAs of tile t+1 overwrite it) and probabilities of alternate tiles.
+    f32x16_t sA[2], sB_own[2];
+    f32x16_t(&sB)[2] = kSpread ? sB_own : sA;
+    u32x4_t pA[4], pB[4];
     Soft sm;
     // after the softmax of a tile: running sum, and the rare rescale of the running output
     auto finish_softmax = [&]() {
@@ -533,9 +556,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         }
     };
     // tile 0: scores, then its softmax on its own
-    stream<D, false, true, false>(w, vbuf(0), kbuf(0), pB, sc, pB, sm);  // S_0
-    mask(sc, next_valid());
-    softmax_all<D>(w, sm, sc, pA);  // P_0 -> pA
+    stream<D, false, true, false>(w, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
+    mask(sA, next_valid());
+    softmax_all<D>(w, sm, sA, pA);  // P_0 -> pA
     finish_softmax();
     __syncthreads();  // every wave is done with K buffer 0 before tile 3 overwrites it
 
@@ -545,38 +568,38 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     // issued NSTAGE - 2 iterations ago) and sync.  K_t is read in iteration t-1 (scores) and
     // V_t in iteration t+1 (P.V), each before the barrier that precedes its buffer's refill.
     // Scores of tile nkt are computed from a stale buffer and never used.  The probability
-    // registers swap roles every iteration (pA <-> pB).
+    // registers swap roles every iteration (pA <-> pB), and so do the score registers.
     // vmcnt(loads issued in the last NSTAGE - 2 iterations)
     constexpr int kWaitPrev = 0x0F70 | ((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE);
     static_assert((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE < 16, "vmcnt field");
-    auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4]) {
+    auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2], f32x16_t(&s_next)[2]) {
         load_k(t + C::NSTAGE);
         load_v(t + C::NSTAGE - 2);
         if (t == 0) {
-            stream<D, false, true, false>(w, vbuf(0), kbuf(1), p_prev, sc, p_cur, sm);
+            stream<D, false, true, false>(w, vbuf(0), kbuf(1), p_prev, s_cur, s_next, p_cur, sm);
         } else {
-            stream<D, true, true, true>(w, vbuf(t - 1), kbuf(t + 1), p_prev, sc, p_cur, sm);
+            stream<D, true, true, true>(w, vbuf(t - 1), kbuf(t + 1), p_prev, s_cur, s_next, p_cur, sm);
             finish_softmax();
         }
-        if (t + 1 < nkt) mask(sc, next_valid());
+        if (t + 1 < nkt) mask(s_next, next_valid());
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
     };
-    iter(0, pB, pA);  // scores S_1
+    iter(0, pB, pA, sA, sB);  // scores S_1 -> sB
     int t = 1;
     for (; t + 1 < nkt; t += 2) {
-        iter(t, pA, pB);      // P.V with P_{t-1} = pA, softmax S_t -> pB
-        iter(t + 1, pB, pA);  // P.V with P_t = pB, softmax S_{t+1} -> pA
+        iter(t, pA, pB, sB, sA);      // P.V with P_{t-1} = pA, softmax S_t (sB) -> pB, S_{t+1} -> sA
+        iter(t + 1, pB, pA, sA, sB);  // P.V with P_t = pB, softmax S_{t+1} (sA) -> pA, S_{t+2} -> sB
     }
     if (t < nkt) {
-        iter(t, pA, pB);
+        iter(t, pA, pB, sB, sA);
         ++t;
     }
     // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)
     if (nkt & 1)
-        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pA, sc, pB, sm);
+        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
     else
-        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pB, sc, pA, sm);
+        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
 
     // ---- epilogue: normalise, LSE, store
     float l0, l1;
