@@ -126,8 +126,10 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
 /*
  * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd needs
  * for this shape, chunk count and merge mode: n fp32 partials (O and LSE) for
- * ATTN_MERGE_NWAY, two for ATTN_MERGE_ONLINE, none for ATTN_MERGE_FUSED or
- * when n_chunks == 1.
+ * ATTN_MERGE_NWAY, two for ATTN_MERGE_ONLINE.  For ATTN_MERGE_FUSED (and any
+ * mode when n_chunks == 1) no partials are needed; the size returned is the
+ * room for splitting the key range of a shape with few query tiles on the
+ * current device (0 when there is nothing to gain).
  * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
  */
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
@@ -147,7 +149,10 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *   flags      one of ATTN_MERGE_NWAY, ATTN_MERGE_ONLINE, ATTN_MERGE_FUSED
  *              (ignored when n_chunks == 1).  FUSED is the ring's loop without
  *              partials: one kernel folds chunk after chunk into its running
- *              max, sum and output.  ONLINE and NWAY run one kernel per chunk
+ *              max, sum and output.  For shapes with few query tiles (bf16) it
+ *              may also split the key tiles over several workgroups per query
+ *              tile and merge their partials, as far as the workspace given
+ *              allows (none given: no split).  ONLINE and NWAY run one kernel per chunk
  *              and merge the fp32 partials with attn_lse_merge's kernel, after
  *              every chunk (as a ring receiving one block per step does) or
  *              once at the end.

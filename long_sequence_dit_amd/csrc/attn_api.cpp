@@ -81,6 +81,44 @@ size_t slot_bytes(int32_t B, int32_t H, int32_t Sq, int32_t D) {
     return align_up(rows * D * 4) + align_up(rows * 4);
 }
 
+constexpr int kMaxSplit = 8;
+
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+// Workgroups per query tile for the bf16 kernel.  1 unless the B*H*ceil(Sq/256) query tiles
+// leave CUs idle in their last round; then the key tiles are split over k workgroups per
+// query tile (k <= kMaxSplit, >= 4 key tiles each), taking the k with the lowest estimated
+// time: the kernel at the CU occupancy k gives, plus (with_merge) writing and merging the k
+// fp32 partials.
+int choose_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int D, int cus, bool with_merge) {
+    const int64_t n_q = B * H * ((Sq + 255) / 256);
+    const int64_t nkt = (Skv + 63) / 64;
+    if (n_q <= 0 || n_q >= 4 * (int64_t)cus) return 1;
+    auto occupancy = [&](int64_t k) {
+        const int64_t wgs = n_q * k, rounds = (wgs + cus - 1) / cus;
+        return (double)wgs / (double)(rounds * cus);
+    };
+    const double flops = 4.0 * (double)B * H * Sq * (double)Skv * D;
+    const double rate = 1.0e15, bw = 5.0e12;  // kernel FLOP/s at full occupancy; merge bytes/s
+    const double rows = (double)B * H * Sq;
+    double best_t = flops / (rate * occupancy(1));
+    int best = 1;
+    for (int k = 2; k <= kMaxSplit && 4 * k <= nkt; ++k) {
+        double t = flops / (rate * occupancy(k));
+        if (with_merge) t += rows * (2.0 * k * (D + 1) * 4 + D * 2 + 4) / bw;
+        if (t < 0.98 * best_t) {
+            best_t = t;
+            best = k;
+        }
+    }
+    return best;
+}
+
 int slots_for(uint32_t flags, int32_t n) {
     if (n <= 1) return 0;
     if (flags == ATTN_MERGE_NWAY) return n;
@@ -116,6 +154,7 @@ attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, at
     a.n_chunks = 1;
     a.chunk_row[0] = 0;
     a.chunk_len[0] = Skv;
+    a.n_split = 1;
     return run_fwd(a, in_dt, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -144,6 +183,11 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
 
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags) {
     if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
+    if (flags == ATTN_MERGE_FUSED || n_chunks == 1) {
+        // room for the key split of few-query-tile shapes (largest split over any key count)
+        const int k = choose_split(B, H, Sq, (int64_t)1 << 40, D, device_cus(), false);
+        return k > 1 ? (size_t)k * slot_bytes(B, H, Sq, D) : 0;
+    }
     const int slots = slots_for(flags, n_chunks);
     if (slots <= 0) return 0;
     return (size_t)slots * slot_bytes(B, H, Sq, D);
@@ -188,7 +232,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     for (int t = 0; t < n_chunks; ++t)
         if (chunk_len[ord[t]] > 0) live[n_live++] = ord[t];
 
-    const size_t need = attn_shard_workspace_size(B, H, Sq, D, n_chunks, flags);
+    const size_t need = slots_for(flags, n_chunks) > 0 ? attn_shard_workspace_size(B, H, Sq, D, n_chunks, flags) : 0;
     if (n_live > 1 && need > 0) {
         if (!workspace || ws_bytes < need) return ATTN_ERR_WORKSPACE;
         if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return ATTN_ERR_ALIGN;
@@ -199,6 +243,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     base.q = q; base.k = k; base.v = v;
     base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
     base.B = B; base.H = H; base.Sq = Sq; base.Skv = (int32_t)total; base.D = D; base.scale = scale;
+    base.n_split = 1;
     auto chunk_args = [&](int c) {  // one chunk, by its rows in the k and v tensors
         FwdArgs a = base;
         a.n_chunks = 1;
@@ -227,8 +272,29 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
             a.chunk_row[t] = (int32_t)off[live[t]];
             a.chunk_len[t] = chunk_len[live[t]];
         }
-        to_final(a);
-        return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        // few query tiles: split the key tiles over k workgroups per query tile, as far as
+        // the workspace allows, and merge the k partials
+        int k = in_dt == ATTN_BF16 ? choose_split(B, H, Sq, total, D, device_cus(), true) : 1;
+        const size_t sb = slot_bytes(B, H, Sq, D);
+        const bool ws_ok = workspace && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0;
+        while (k > 1 && (!ws_ok || ws_bytes < (size_t)k * sb)) --k;
+        if (k == 1) {
+            to_final(a);
+            return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        }
+        a.n_split = k;
+        a.o = slot_o(0); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(0);
+        a.split_o_stride = a.split_lse_stride = (int64_t)(sb / 4);
+        if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
+        MergeArgs m{};
+        m.B = B; m.H = H; m.Sq = Sq; m.D = D;
+        m.n = k;
+        for (int i = 0; i < k; ++i) {
+            m.o_parts[i] = slot_o(i);
+            m.lse_parts[i] = slot_lse(i);
+        }
+        m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
+        return ok(lsdit::launch_lse_merge(m, s)) ? ATTN_OK : ATTN_ERR_HIP;
     }
 
     MergeArgs m{};

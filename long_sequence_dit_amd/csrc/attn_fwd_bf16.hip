@@ -203,6 +203,17 @@ struct TileWalk {
         if (row >= end) enter(c + 1, n_chunks, v_row, v_len, past);
     }
     __device__ __forceinline__ int valid() const { return end - row; }  // >= BK: a full tile
+    // Tile g of the sequence (a scalar walk over the chunks' tile counts).
+    __device__ __forceinline__ void seek(int g, int n_chunks, int v_row, int v_len, int past) {
+        int ci = 0;
+        for (; ci < n_chunks; ++ci) {
+            const int nt = (__builtin_amdgcn_readlane(v_len, ci) + BK - 1) / BK;
+            if (g < nt) break;
+            g -= nt;
+        }
+        enter(ci, n_chunks, v_row, v_len, past);
+        if (ci < n_chunks) row += g * BK;
+    }
 };
 
 // Per-wave state of the key loop.
@@ -412,7 +423,11 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hi = lane >> 5;  // which half of the wave (MFMA k-half)
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    // grid = n_split groups of B*H*n_qt query tiles; the split index varies slowest, so each
+    // XCD's contiguous share of the remapped grid reads one key range of few heads
+    const int gidx = xcd_remap(blockIdx.x, gridDim.x);
+    const int n_qtiles = a.B * a.H * n_qt;
+    const int split = gidx / n_qtiles, tile = gidx % n_qtiles;
     const int bh = tile / n_qt, qt = tile % n_qt;
     const int b = bh / a.H, h = bh % a.H;
 
@@ -430,8 +445,11 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         (const int*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(FwdArgs, chunk_len));
     const int v_row = lane < n_chunks ? arg_rows[lane] : 0;
     const int v_len = lane < n_chunks ? arg_lens[lane] : 0;
-    int nkt = 0;  // tiles over all chunks
-    for (int ci = 0; ci < n_chunks; ++ci) nkt += (__builtin_amdgcn_readlane(v_len, ci) + C::BK - 1) / C::BK;
+    int nkt_all = 0;  // tiles over all chunks
+    for (int ci = 0; ci < n_chunks; ++ci) nkt_all += (__builtin_amdgcn_readlane(v_len, ci) + C::BK - 1) / C::BK;
+    // this workgroup's share of the tile sequence
+    const int g_first = (int)((int64_t)split * nkt_all / a.n_split);
+    const int nkt = (int)((int64_t)(split + 1) * nkt_all / a.n_split) - g_first;
 
     Wave<D> w;
     w.c = c;
@@ -477,7 +495,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     // iteration t), the next V tile to load (tile t + NSTAGE - 2) and the next tile to mask
     // (tile t + 1).  Tile g of the sequence goes into buffer g mod NSTAGE.
     TileWalk<C::BK> wk, wv, wm;
-    wk.enter(0, n_chunks, v_row, v_len, Skv);
+    wk.seek(g_first, n_chunks, v_row, v_len, Skv);
     wv = wk;
     wm = wk;
     auto load_k = [&](int g) {
@@ -609,7 +627,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
     if (qrow < a.Sq) {
         if (a.o_bf16) {
-            unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
+            unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;  // no split
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -621,7 +639,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                     *(u32x2_t*)(op + d) = wd;
                 }
         } else {
-            float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
+            float* op = (float*)a.o + split * a.split_o_stride + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -633,7 +651,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                     *(f32x4_t*)(op + d) = x;
                 }
         }
-        if (hi == 0) a.lse[(int64_t)bh * a.Sq + qrow] = lse2 * kLn2;
+        if (hi == 0) a.lse[split * a.split_lse_stride + (int64_t)bh * a.Sq + qrow] = lse2 * kLn2;
     }
 }
 
@@ -651,7 +669,8 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
         if (dev >= 0 && dev < 64) attr_set[dev] = true;
     }
     const int n_qt = (a.Sq + C::BQ - 1) / C::BQ;
-    const int64_t n_tiles = (int64_t)a.B * a.H * n_qt;
+    if (a.n_split < 1 || (a.n_split > 1 && a.o_bf16)) return hipErrorInvalidValue;
+    const int64_t n_tiles = (int64_t)a.B * a.H * n_qt * a.n_split;
     if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const float c = (float)((double)a.scale * 1.4426950408889634);
     hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)n_tiles), dim3(C::NT), C::LDS_BYTES, stream, a, n_qt, c);

@@ -31,6 +31,12 @@ struct FwdArgs {
     int n_chunks;        // 1 .. kMaxChunks
     int chunk_row[kMaxChunks];
     int chunk_len[kMaxChunks];  // each > 0
+    // Split over the keys (bf16 path): n_split > 1 launches n_split workgroups per query
+    // tile; split s takes tiles [s*T/n_split, (s+1)*T/n_split) of the T key tiles and writes
+    // an fp32 partial (normalised by its own row sum) and its LSE at o + s*split_o_stride and
+    // lse + s*split_lse_stride (elements); the partials are then merged by their LSE.
+    int n_split;         // 1 = no split
+    int64_t split_o_stride, split_lse_stride;
 };
 
 // Merge of up to kMaxMergeParts fp32 partials (contiguous [B,H,Sq,D] / [B,H,Sq]).

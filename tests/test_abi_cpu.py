@@ -151,7 +151,12 @@ def test_workspace_sizes(attn):
     slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot   # n-way
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 2 * slot   # online
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == 0          # fused: no partials
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == 0
+    # fused: no chunk partials; a shape with few query tiles (16 heads x 22 tiles of 256 rows,
+    # fewer than the GPU's CUs can run in full rounds) gets room to split its key range over
+    # 2..8 workgroups per query tile, a shape with many query tiles none
+    ws = lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4)
+    assert ws % slot == 0 and 2 <= ws // slot <= 8, ws / slot
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == ws  # one chunk: same kernel
+    assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0

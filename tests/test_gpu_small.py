@@ -121,6 +121,23 @@ def test_max_chunks_random_lengths_and_order(dtype, mode):
     assert_parity(o, l, o_ref, l_ref, fp32=dtype == "fp32", what="64 chunks %s %s" % (dtype, mode))
 
 
+@pytest.mark.parametrize("Skv", [260, 512, 3000])
+def test_key_split_matches_unsplit(Skv):
+    """Few query tiles: the fused schedule splits the key tiles over several workgroups per
+    query tile when given the workspace (and runs unsplit without it); both match the oracle."""
+    B, H, Sq, D = 1, 3, 200, 128
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=21)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    lens = (Skv // 3, Skv - Skv // 3)
+    need = A().shard_workspace_size(B, H, Sq, D, len(lens), "fused")
+    assert need > 0  # 3 query tiles: room for a split
+    for ws in (torch.empty(need, dtype=torch.uint8, device="cuda"), torch.empty(0, dtype=torch.uint8, device="cuda")):
+        o, l = A().shard_fwd(qd, kd, vd, lens, (1, 0), mode="fused", workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(o, l, o_ref, l_ref, what="Skv %d workspace %d" % (Skv, ws.numel()))
+
+
 def test_bf16_chunk_partials_and_merge():
     B, H, Sq, D = 1, 2, 200, 128
     lens = (70, 130, 64)
