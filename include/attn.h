@@ -168,6 +168,33 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
                              uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
                              attn_dtype_t o_dt, float* lse, attn_stream_t stream);
 
+/*
+ * attn_ulysses_pack / attn_ulysses_unpack — the local halves of the all-to-all
+ * around DeepSpeed-Ulysses attention (blog section "DeepSpeed Ulysses": each
+ * rank trades its sequence slice of all heads for the whole sequence of a
+ * subset of heads, and trades back after attention).
+ *
+ *   pack:   packed[j][s][b][h'][d] = x[b][j*Hg + h'][s][d]
+ *   unpack: x[b][j*Hg + h'][s][d]  = packed[j][s][b][h'][d]
+ *
+ *   x       [B, H, S, D] in dt, strides xs (d stride 1): a rank's sequence
+ *           slice, or on one GPU the whole sequence
+ *   packed  [n][S][B][Hg][D] in dt, contiguous, Hg = H / n: part j is what
+ *           goes to (pack) or came from (unpack) rank j
+ *   dt      ATTN_BF16 or ATTN_F32; n >= 1 with H % n == 0
+ * Because each part is in [S, B, Hg, D] order, the parts rank j receives from
+ * ranks 0..n-1 (consecutive sequence slices) concatenate into head group j over
+ * the whole sequence, which attn_chunk_fwd and attn_shard_fwd read as a strided
+ * [B, Hg, S_total, D] view: b stride Hg*D, h stride D, s stride B*Hg*D.  On one
+ * GPU, packing the whole sequence gives every head group's input directly.
+ * x and packed must not overlap.  Same pointer/stride alignment rules and
+ * error behaviour as the other entry points; S = 0 or B = 0 is a no-op.
+ */
+attn_status_t attn_ulysses_pack(const void* x, attn_strides_t xs, attn_dtype_t dt, int32_t B, int32_t H, int32_t S,
+                                int32_t D, int32_t n, void* packed, attn_stream_t stream);
+attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B, int32_t H, int32_t S, int32_t D,
+                                  int32_t n, void* x, attn_strides_t xs, attn_stream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status_t s);
 

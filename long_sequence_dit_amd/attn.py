@@ -31,7 +31,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DT
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_chunk_fwd", "attn_lse_merge", "attn_shard_workspace_size", "attn_shard_fwd",
-           "attn_status_str", "attn_abi_version")
+           "attn_ulysses_pack", "attn_ulysses_unpack", "attn_status_str", "attn_abi_version")
 
 
 class Strides(ctypes.Structure):
@@ -68,6 +68,10 @@ def load():
         lib.attn_shard_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, ctypes.c_int, i32, i32, i32, i32, f32,
                                        i32, vp, vp, u32, vp, sz, vp, Strides, ctypes.c_int, vp, vp]
         lib.attn_shard_fwd.restype = ctypes.c_int
+        lib.attn_ulysses_pack.argtypes = [vp, Strides, ctypes.c_int, i32, i32, i32, i32, i32, vp, vp]
+        lib.attn_ulysses_pack.restype = ctypes.c_int
+        lib.attn_ulysses_unpack.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, i32, vp, Strides, vp]
+        lib.attn_ulysses_unpack.restype = ctypes.c_int
         lib.attn_status_str.argtypes = [ctypes.c_int]
         lib.attn_status_str.restype = ctypes.c_char_p
         lib.attn_abi_version.argtypes = []
@@ -198,3 +202,38 @@ def shard_fwd(q, k, v, chunk_lens: Sequence[int], order: Optional[Sequence[int]]
                                _stream_ptr(stream))
     _check(rc, "attn_shard_fwd")
     return out, lse
+
+
+def ulysses_pack(x, n: int, packed=None, stream=None):
+    """Head groups of x [B, H, S, D] -> packed [n, S, B, H/n, D] (part j goes to rank j)."""
+    B, H, S, D = x.shape
+    if H % n:
+        raise ValueError("H must be a multiple of n")
+    if packed is None:
+        packed = torch.empty((n, S, B, H // n, D), dtype=x.dtype, device=x.device)
+    if not packed.is_contiguous() or packed.dtype != x.dtype or tuple(packed.shape) != (n, S, B, H // n, D):
+        raise ValueError("packed must be contiguous [n, S, B, H/n, D] of x's dtype")
+    rc = load().attn_ulysses_pack(x.data_ptr(), _bhsd(x, "x"), _dt(x), B, H, S, D, n, packed.data_ptr(),
+                                  _stream_ptr(stream))
+    _check(rc, "attn_ulysses_pack")
+    return packed
+
+
+def ulysses_unpack(packed, out=None, stream=None):
+    """packed [n, S, B, Hg, D] -> [B, n*Hg, S, D] (or into `out`, any [B, H, S, D] view)."""
+    n, S, B, Hg, D = packed.shape
+    if not packed.is_contiguous():
+        raise ValueError("packed must be contiguous")
+    if out is None:
+        out = torch.empty((B, n * Hg, S, D), dtype=packed.dtype, device=packed.device)
+    if tuple(out.shape) != (B, n * Hg, S, D) or out.dtype != packed.dtype:
+        raise ValueError("out must be [B, n*Hg, S, D] of packed's dtype")
+    rc = load().attn_ulysses_unpack(packed.data_ptr(), _dt(packed), B, n * Hg, S, D, n, out.data_ptr(),
+                                    _bhsd(out, "out"), _stream_ptr(stream))
+    _check(rc, "attn_ulysses_unpack")
+    return out
+
+
+def head_group_view(packed, j: int):
+    """Part j of a packed buffer ([S, B, Hg, D]) as the [B, Hg, S, D] view attention takes."""
+    return packed[j].permute(1, 2, 0, 3)

@@ -332,6 +332,34 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     return ok(lsdit::launch_lse_merge(m, s)) ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+namespace {
+
+attn_status_t relayout(const void* src, void* dst, attn_strides_t xs, attn_dtype_t dt, int32_t B,
+                       int32_t H, int32_t S, int32_t D, int32_t n, bool pack, hipStream_t stream) {
+    if (!valid_dtype(dt)) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || S < 0 || n < 1 || H % n != 0) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * S == 0) return ATTN_OK;
+    if (!src || !dst) return ATTN_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || !strides_ok(xs, esize(dt))) return ATTN_ERR_ALIGN;
+    lsdit::RelayoutArgs a{};
+    a.src = src; a.dst = dst; a.st = Strides{xs.b, xs.h, xs.s};
+    a.n = n; a.B = B; a.S = S; a.Hg = H / n; a.D = D; a.esize = (int)esize(dt);
+    return lsdit::launch_ulysses_relayout(a, pack, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+attn_status_t attn_ulysses_pack(const void* x, attn_strides_t xs, attn_dtype_t dt, int32_t B, int32_t H, int32_t S,
+                                int32_t D, int32_t n, void* packed, attn_stream_t stream) {
+    return relayout(x, packed, xs, dt, B, H, S, D, n, true, (hipStream_t)stream);
+}
+
+attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B, int32_t H, int32_t S, int32_t D,
+                                  int32_t n, void* x, attn_strides_t xs, attn_stream_t stream) {
+    return relayout(packed, x, xs, dt, B, H, S, D, n, false, (hipStream_t)stream);
+}
+
 const char* attn_status_str(attn_status_t s) {
     switch (s) {
         case ATTN_OK: return "ok";

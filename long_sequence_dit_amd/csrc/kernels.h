@@ -52,11 +52,23 @@ struct MergeArgs {
     float* lse;
 };
 
+// Ulysses re-layout between a strided [B, H, S, D] tensor (strides st, unit d stride) and the
+// packed [n][S][B][Hg][D] buffer (Hg = H / n) whose part j goes to, or came from, rank j.
+struct RelayoutArgs {
+    const void* src;
+    void* dst;
+    Strides st;          // of the strided side (elements)
+    int n, B, S, Hg, D;  // H = n * Hg
+    int esize;           // bytes per element (2 or 4)
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 // O = 0 and LSE = -inf for every row (a chunk without keys).
+// pack: src strided -> dst packed; unpack: src packed -> dst strided.
+hipError_t launch_ulysses_relayout(const RelayoutArgs& a, bool pack, hipStream_t stream);
 hipError_t launch_fill_empty(void* o, Strides os, int o_bf16, float* lse, int B, int H, int Sq, int D,
                              hipStream_t stream);
 

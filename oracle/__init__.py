@@ -130,3 +130,30 @@ def chunk_partials(q, k, v, scale, chunk_lens: Sequence[int], q_rows=None, nthre
         off += n
     assert off == k.shape[2]
     return out
+
+
+# ---- DeepSpeed-Ulysses re-layout (blog section "DeepSpeed Ulysses": each rank trades its
+# sequence slice of all heads for the whole sequence of one head group).  Pure data movement;
+# the definitions below are index maps, exact for any dtype.
+
+def ulysses_pack(x: np.ndarray, n: int) -> np.ndarray:
+    """x [B, H, S, D] -> packed [n, S, B, H/n, D] with packed[j, s, b, h', d] = x[b, j*H/n + h', s, d]."""
+    B, H, S, D = x.shape
+    assert H % n == 0
+    Hg = H // n
+    out = np.empty((n, S, B, Hg, D), dtype=x.dtype)
+    for j in range(n):
+        for b in range(B):
+            # head group j of batch b, [Hg, S, D] -> [S, Hg, D]
+            out[j, :, b] = np.transpose(x[b, j * Hg:(j + 1) * Hg], (1, 0, 2))
+    return out
+
+
+def ulysses_unpack(packed: np.ndarray) -> np.ndarray:
+    """packed [n, S, B, Hg, D] -> x [B, n*Hg, S, D], the inverse of ulysses_pack."""
+    n, S, B, Hg, D = packed.shape
+    x = np.empty((B, n * Hg, S, D), dtype=packed.dtype)
+    for j in range(n):
+        for b in range(B):
+            x[b, j * Hg:(j + 1) * Hg] = np.transpose(packed[j, :, b], (1, 0, 2))
+    return x

@@ -160,3 +160,21 @@ def test_workspace_sizes(attn):
     assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0
+
+
+def test_ulysses_relayout_argument_errors(attn):
+    lib = attn.load()
+    c = _st(4 * 8 * 128, 8 * 128, 128)
+    pack = lambda **kw: lib.attn_ulysses_pack(kw.get("x", P), kw.get("xs", c), kw.get("dt", BF16), kw.get("B", 1),
+                                              kw.get("H", 8), kw.get("S", 4), kw.get("D", 128), kw.get("n", 4),
+                                              kw.get("out", P), None)
+    unpack = lambda **kw: lib.attn_ulysses_unpack(kw.get("inp", P), kw.get("dt", BF16), 1, kw.get("H", 8), 4, 128,
+                                                  kw.get("n", 4), kw.get("x", P), kw.get("xs", c), None)
+    assert pack(dt=9) == DTYPE
+    assert pack(D=96) == UNSUP
+    assert pack(n=3) == SHAPE and pack(n=0) == SHAPE and pack(H=-8) == SHAPE
+    assert pack(x=None) == NULL and pack(out=None) == NULL
+    assert pack(x=P + 8) == ALIGN and pack(xs=_st(0, 0, 4)) == ALIGN
+    assert pack(x=None, out=None, S=0) == OK and pack(x=None, out=None, B=0) == OK
+    assert unpack(dt=9) == DTYPE and unpack(n=3) == SHAPE
+    assert unpack(inp=None) == NULL and unpack(x=P + 8) == ALIGN

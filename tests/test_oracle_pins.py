@@ -255,3 +255,43 @@ def test_row_selection_matches_full_rows():
     assert np.array_equal(os_, o[:, :, rows]) and np.array_equal(ls_, lse[:, :, rows])
     oz, lz = oracle.attention(q[:, :, :0], k, v, 0.25)
     assert oz.shape == (1, 2, 0, 16) and lz.shape == (1, 2, 0)
+
+
+# ---- Ulysses re-layout: pinned by brute force over every index, by the exchange property the
+# layout exists for, and by the round trip.
+
+def test_ulysses_pack_brute_force_indices():
+    rng = np.random.default_rng(3)
+    B, H, S, D, n = 2, 6, 5, 4, 3
+    x = rng.standard_normal((B, H, S, D))
+    p = oracle.ulysses_pack(x, n)
+    assert p.shape == (n, S, B, H // n, D)
+    for j in range(n):
+        for s in range(S):
+            for b in range(B):
+                for hq in range(H // n):
+                    for d in range(D):
+                        assert p[j, s, b, hq, d] == x[b, j * (H // n) + hq, s, d]
+
+
+def test_ulysses_exchange_concatenates_rank_slices():
+    """Rank r packs its sequence slice; rank j receives part j from every rank.  Concatenating
+    those parts by source rank equals part j of packing the whole sequence at once."""
+    rng = np.random.default_rng(4)
+    B, H, S, D, n = 2, 8, 12, 4, 4
+    x = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    whole = oracle.ulysses_pack(x, n)
+    sl = S // n
+    per_rank = [oracle.ulysses_pack(x[:, :, r * sl:(r + 1) * sl], n) for r in range(n)]
+    for j in range(n):
+        received = np.concatenate([per_rank[r][j] for r in range(n)], axis=0)  # [S, B, Hg, D]
+        assert np.array_equal(received, whole[j])
+
+
+def test_ulysses_round_trip_and_single_group():
+    rng = np.random.default_rng(5)
+    x = rng.integers(0, 2**16, size=(1, 4, 7, 8), dtype=np.uint16)  # bf16 bit patterns
+    for n in (1, 2, 4):
+        assert np.array_equal(oracle.ulysses_unpack(oracle.ulysses_pack(x, n)), x)
+    # one group: the packed part is x with its S and H axes moved
+    assert np.array_equal(oracle.ulysses_pack(x, 1)[0], np.transpose(x, (2, 0, 1, 3)))
