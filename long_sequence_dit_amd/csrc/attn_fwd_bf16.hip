@@ -200,7 +200,12 @@ struct TileWalk {
     }
     __device__ __forceinline__ void next(int n_chunks, int v_row, int v_len, int past) {
         row += BK;
-        if (row >= end) enter(c + 1, n_chunks, v_row, v_len, past);
+        if (row >= end) {
+            // keeps the chunk-table reads (VALU readlanes) behind the branch: hoisted, they
+            // would run on every tile
+            asm volatile("");
+            enter(c + 1, n_chunks, v_row, v_len, past);
+        }
     }
     __device__ __forceinline__ int valid() const { return end - row; }  // >= BK: a full tile
     // Tile g of the sequence (a scalar walk over the chunks' tile counts).
@@ -256,9 +261,10 @@ struct Soft {
 // the next tile overwrite them.
 __host__ __device__ constexpr int pair_slot(int j, int la) { return 5 + j * (la - 4) / 16; }
 
-// Empty asm statements (register operands only) pin a stage to its slot: the scheduling
-// barriers order instructions, but pure arithmetic could still be hoisted above them or
-// sunk towards its use.
+// Empty asm statements (register operands only) pin a stage's results to its slot: the
+// scheduling barriers order instructions, but pure arithmetic could still be sunk towards
+// its use.  Only results are pinned: pinning an input read out of a live score vector would
+// make the compiler copy it first (one move per input).
 __device__ __forceinline__ void pin(float& a, float& b) { asm volatile("" : "+v"(a), "+v"(b)); }
 
 template <int POS, int LA, int J = 0>
@@ -266,8 +272,7 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
     if constexpr (J < 16) {
         constexpr int a = pair_slot(J, LA);
         if constexpr (POS == a) {
-            float x0 = s[J >> 3][2 * (J & 7)], x1 = s[J >> 3][2 * (J & 7) + 1];
-            pin(x0, x1);
+            const float x0 = s[J >> 3][2 * (J & 7)], x1 = s[J >> 3][2 * (J & 7) + 1];
             sm.x[J][0] = __builtin_fmaf(x0, c, -sm.m_new);
             sm.x[J][1] = __builtin_fmaf(x1, c, -sm.m_new);
             pin(sm.x[J][0], sm.x[J][1]);
