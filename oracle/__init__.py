@@ -5,6 +5,8 @@ wrapper.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
 of ``bench.py`` may import this package; the GPU library never does, and the
 two share no code.  Inputs are numpy arrays: float64, float32, or uint16
 holding bf16 bit patterns; the C side widens each element exactly to fp64.
+FP8 (OCP E4M3) inputs are decoded to fp64 here (``e4m3_decode``) and scaled
+by their per-tensor descales before the same attention.
 
 Every function follows the plain definition of bidirectional multi-head
 softmax attention (NVIDIA Technical Blog "Scaling AI Inference Across
@@ -157,3 +159,32 @@ def ulysses_unpack(packed: np.ndarray) -> np.ndarray:
         for b in range(B):
             x[b, j * Hg:(j + 1) * Hg] = np.transpose(packed[j, :, b], (1, 0, 2))
     return x
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64, exactly.
+
+    Sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.  Exponent
+    field 0: (-1)^s * m * 2^-9 (zero and subnormals); otherwise
+    (-1)^s * (1 + m/8) * 2^(e-7).  Codes 0x7F and 0xFF are NaN; the format has
+    no infinities.  Straight from the format definition, element by element.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+def attention_e4m3(q, k, v, q_descale: float, k_descale: float, v_descale: float, scale: float,
+                   q_rows=None, nthreads: int = 0):
+    """Attention of E4M3-coded tensors: the plain definition applied to the decoded
+    values times their per-tensor descales (each product exact in fp64)."""
+    if q_rows is not None:
+        q = q[:, :, np.asarray(q_rows, dtype=np.int64), :]
+    qd = e4m3_decode(q) * float(q_descale)
+    kd = e4m3_decode(k) * float(k_descale)
+    vd = e4m3_decode(v) * float(v_descale)
+    return attention(qd, kd, vd, scale, nthreads=nthreads)

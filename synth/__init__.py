@@ -112,6 +112,48 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r
 
 
+E4M3_MAX = 448.0
+
+
+def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Values -> OCP FP8 E4M3 codes (uint8) by round-to-nearest-even.
+
+    E4M3 (the "fn" variant): sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent field 0 holds subnormals m * 2^-9; no infinities, and codes
+    0x7F / 0xFF are NaN, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    Every finite input must round to a magnitude <= 448 (scale inputs into
+    range first); anything else raises.
+
+    Within binade [2^e, 2^(e+1)), e >= -6, representable magnitudes are the
+    multiples of 2^(e-3); below 2^-6 the step stays 2^-9.  With e clamped to
+    >= -6 and q = round-half-even(|x| / 2^(e-3)), the code is 8 (e + 6) + q
+    (a q of 16 carries into the next binade by the same formula).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("E4M3 encoding of a non-finite value")
+    a = np.abs(x)
+    _, ex = np.frexp(a)                      # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    q = np.rint(np.ldexp(a, (3 - e).astype(np.int32))).astype(np.int64)  # exact scaling, RNE
+    code = 8 * (e + 6) + q
+    code = np.where(a == 0.0, 0, code)
+    if np.any(code > 0x7E):
+        raise ValueError("E4M3 encoding: magnitude beyond 448 after rounding")
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def e4m3_quantize(x: np.ndarray):
+    """Per-tensor E4M3 quantization: (codes, descale) with x ~= decode(codes) * descale.
+
+    descale = max|x| / 448 in fp32, so the largest magnitude maps to 448.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    return f64_to_e4m3_bits(x / descale), descale
+
+
 def outlier_rows(seed: int, S: int, count: int) -> np.ndarray:
     """`count` distinct row positions in [0, S), drawn without replacement.
 

@@ -99,6 +99,29 @@ class Workload:
         return {"q": q, "k": k, "v": v}
 
 
+    def make_inputs_fp8(self, seed: int = 0) -> Dict[str, object]:
+        """E4M3 codes (uint8, [B, H, S, D]) of the same draws as make_inputs, each tensor
+        quantized per tensor from its fp32 values; descales in "q_descale" etc."""
+        s_full = self.s_full or self.Sq
+        src = {
+            "q": synth.normal_rows(seed, synth.TID_Q, self.B, self.H, s_full, self.D, self.q_row_lo,
+                                   self.q_row_lo + self.Sq, self.qk_factor, None, synth.KIND_F32),
+        }
+        row_factor = None
+        if self.outlier_count:
+            row_factor = np.ones(self.Skv)
+            row_factor[self.outlier_positions(seed)] = self.outlier_factor
+        src["k"] = synth.normal_rows(seed, synth.TID_K, self.B, self.H, self.Skv, self.D, 0, self.Skv,
+                                     self.qk_factor, row_factor, synth.KIND_F32)
+        src["v"] = synth.normal_rows(seed, synth.TID_V, self.B, self.H, self.Skv, self.D, 0, self.Skv, 1.0, None,
+                                     synth.KIND_F32)
+        out: Dict[str, object] = {}
+        for name, x in src.items():
+            codes, descale = synth.e4m3_quantize(x)
+            out[name] = codes
+            out[name + "_descale"] = descale
+        return out
+
 def _even_plans(total: int, counts) -> Dict[str, ChunkPlan]:
     return {"chunks%d" % n: ChunkPlan(tuple(even_chunks(total, n))) for n in counts}
 

@@ -295,3 +295,73 @@ def test_ulysses_round_trip_and_single_group():
         assert np.array_equal(oracle.ulysses_unpack(oracle.ulysses_pack(x, n)), x)
     # one group: the packed part is x with its S and H axes moved
     assert np.array_equal(oracle.ulysses_pack(x, 1)[0], np.transpose(x, (2, 0, 1, 3)))
+
+
+# ---- FP8 (OCP E4M3) decoding of the oracle and encoding of the input generator.
+# The values below are fixed by the E4M3 format definition (bias 7, 3 mantissa bits,
+# subnormal step 2^-9, largest finite 1.75 * 2^8, 0x7F/0xFF NaN, no infinities).
+
+E4M3_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+              0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3C: 1.5, 0x40: 2.0, 0x44: 3.0, 0x58: 16.0, 0x59: 18.0,
+              0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0x81: -(2.0 ** -9), 0xB8: -1.0, 0xFE: -448.0}
+
+
+def test_e4m3_decode_format_values():
+    codes = np.array(sorted(E4M3_KNOWN), dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(got, np.array([E4M3_KNOWN[int(c)] for c in codes]))
+    assert np.signbit(oracle.e4m3_decode(np.array([0x80], np.uint8))[0])
+    assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    # every finite positive code decodes to a strictly larger value than the one before it
+    pos = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0) and pos[-1] == 448.0
+
+
+def test_e4m3_encode_round_trip_and_ties_to_even():
+    import synth
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    assert np.array_equal(synth.f64_to_e4m3_bits(vals), codes)
+    # midpoints of neighbouring codes round to the even code (even mantissa), and values
+    # just off the midpoint round to the nearer code
+    lo = np.arange(0, 0x7E, dtype=np.uint8)
+    a, b = oracle.e4m3_decode(lo), oracle.e4m3_decode(lo + 1)
+    mid = (a + b) / 2
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(synth.f64_to_e4m3_bits(mid), even)
+    assert np.array_equal(synth.f64_to_e4m3_bits(np.nextafter(mid, 0)), lo)
+    assert np.array_equal(synth.f64_to_e4m3_bits(np.nextafter(mid, 1e9)), lo + 1)
+    assert np.array_equal(synth.f64_to_e4m3_bits(-mid), even | 0x80)
+    with pytest.raises(ValueError):
+        synth.f64_to_e4m3_bits(np.array([464.0 + 1e-9]))
+    with pytest.raises(ValueError):
+        synth.f64_to_e4m3_bits(np.array([np.inf]))
+
+
+def test_e4m3_quantize_relative_error_and_range():
+    import synth
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(4096) * 3.0
+    codes, descale = synth.e4m3_quantize(x)
+    back = oracle.e4m3_decode(codes) * descale
+    assert np.max(np.abs(oracle.e4m3_decode(codes))) == 448.0
+    normal = np.abs(x) >= 2.0 ** -6 * descale
+    # round-to-nearest with 3 mantissa bits: relative error at most 2^-4 in the normal range
+    assert np.all(np.abs(back - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] * (1 + 1e-12))
+    assert np.all(np.abs(back - x)[~normal] <= 2.0 ** -10 * descale * (1 + 1e-12))
+
+
+def test_attention_e4m3_is_attention_of_decoded_values():
+    # small integer codes with power-of-two descales: the decoded inputs are exact, so the
+    # fp8 entry must equal the plain attention on the same values
+    rng = np.random.default_rng(6)
+    q8, k8, v8 = (rng.choice(np.array([0x30, 0x38, 0x3C, 0x40, 0xB0, 0xB8, 0xC0], np.uint8), size=(1, 2, 5, 8))
+                  for _ in range(3))
+    o, lse = oracle.attention_e4m3(q8, k8, v8, 0.5, 2.0, 0.25, 0.3)
+    qd, kd, vd = (oracle.e4m3_decode(x) * s for x, s in ((q8, 0.5), (k8, 2.0), (v8, 0.25)))
+    s = np.einsum("bhid,bhjd->bhij", qd, kd) * 0.3
+    w = np.exp(s - s.max(-1, keepdims=True))
+    assert np.allclose(o, np.einsum("bhij,bhjd->bhid", w / w.sum(-1, keepdims=True), vd), rtol=1e-13, atol=1e-14)
+    assert np.allclose(lse, np.log(w.sum(-1)) + s.max(-1), rtol=1e-13, atol=1e-14)
+    o2, lse2 = oracle.attention_e4m3(q8, k8, v8, 0.5, 2.0, 0.25, 0.3, q_rows=[4, 1])
+    assert np.array_equal(o2, o[:, :, [4, 1]]) and np.array_equal(lse2, lse[:, :, [4, 1]])
