@@ -195,6 +195,39 @@ attn_status_t attn_ulysses_pack(const void* x, attn_strides_t xs, attn_dtype_t d
 attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B, int32_t H, int32_t S, int32_t D,
                                   int32_t n, void* x, attn_strides_t xs, attn_stream_t stream);
 
+/*
+ * attn_chunk_fwd_fp8 — the FP8 variant of attn_chunk_fwd: attention of every
+ * query row against one chunk of keys, on OCP FP8 E4M3 inputs (8-bit floats,
+ * which suit attention layers: page "TensorRT Multi-Device Inference:
+ * Engineering Practices for Breaking Through Single-GPU Memory Bottlenecks",
+ * section "Why a Single GPU Is No Longer Enough").
+ *
+ *   q, k, v  E4M3 codes, one byte per element, [B,H,Sq,D] / [B,H,Skv,D] with
+ *            strides qs, ks, vs in elements (= bytes), d stride 1; the values
+ *            are code * q_descale (k_descale, v_descale), descales finite > 0
+ *   D        128 only (else ATTN_ERR_UNSUPPORTED)
+ *   o, lse   as attn_chunk_fwd: O in o_dt (ATTN_BF16 or ATTN_F32), natural-log
+ *            LSE fp32 [B,H,Sq] contiguous, scale included
+ *   workspace  device scratch of at least attn_fp8_workspace_size(B,H,Skv,D)
+ *            bytes, 16-byte aligned, owned by the caller; it receives V
+ *            re-laid out as transposed 64-key tiles and may be reused once the
+ *            call's work on `stream` has finished
+ * The probabilities enter P.V as E4M3 (after scaling by 2^5), so the result
+ * differs from exact attention of the decoded inputs by up to 2^-4 of the
+ * probability-weighted mean of |V| per element (relative rounding of each
+ * probability); the row sum adds the same rounded probabilities.
+ * Pointers must be 16-byte aligned and b/h/s strides multiples of 16 bytes
+ * (ATTN_ERR_ALIGN); one head's K rows must span under 2 GiB and Skv < 2^23
+ * (ATTN_ERR_UNSUPPORTED); a short workspace gives ATTN_ERR_WORKSPACE.
+ * Sq = 0, B = 0 or H = 0 is a no-op; Skv = 0 gives O = 0, LSE = -inf.
+ */
+size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Skv, int32_t D);
+attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                                 attn_strides_t vs, float q_descale, float k_descale, float v_descale, int32_t B,
+                                 int32_t H, int32_t Sq, int32_t Skv, int32_t D, float scale, void* workspace,
+                                 size_t ws_bytes, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                                 attn_stream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_str(attn_status_t s);
 

@@ -31,7 +31,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DT
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_chunk_fwd", "attn_lse_merge", "attn_shard_workspace_size", "attn_shard_fwd",
-           "attn_ulysses_pack", "attn_ulysses_unpack", "attn_status_str", "attn_abi_version")
+           "attn_ulysses_pack", "attn_ulysses_unpack", "attn_fp8_workspace_size", "attn_chunk_fwd_fp8",
+           "attn_status_str", "attn_abi_version")
 
 
 class Strides(ctypes.Structure):
@@ -72,6 +73,11 @@ def load():
         lib.attn_ulysses_pack.restype = ctypes.c_int
         lib.attn_ulysses_unpack.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, i32, vp, Strides, vp]
         lib.attn_ulysses_unpack.restype = ctypes.c_int
+        lib.attn_fp8_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.attn_fp8_workspace_size.restype = sz
+        lib.attn_chunk_fwd_fp8.argtypes = [vp, Strides, vp, Strides, vp, Strides, f32, f32, f32, i32, i32, i32, i32,
+                                           i32, f32, vp, sz, vp, Strides, ctypes.c_int, vp, vp]
+        lib.attn_chunk_fwd_fp8.restype = ctypes.c_int
         lib.attn_status_str.argtypes = [ctypes.c_int]
         lib.attn_status_str.restype = ctypes.c_char_p
         lib.attn_abi_version.argtypes = []
@@ -139,6 +145,44 @@ def chunk_fwd(q, k, v, scale=None, out=None, lse=None, out_dtype=None, stream=No
                                _bhsd(v, "v"), _dt(q), B, H, Sq, Skv, D, _scale(scale, D), out.data_ptr(),
                                _bhsd(out, "out"), _dt(out), lse.data_ptr(), _stream_ptr(stream))
     _check(rc, "attn_chunk_fwd")
+    return out, lse
+
+
+def fp8_workspace_size(B, H, Skv, D) -> int:
+    return int(load().attn_fp8_workspace_size(B, H, Skv, D))
+
+
+def _e4m3(t: torch.Tensor, name: str) -> torch.Tensor:
+    """E4M3 codes as a uint8 view (torch.float8_e4m3fn tensors are accepted as they are)."""
+    if t.dtype == torch.uint8:
+        return t
+    if t.dtype == getattr(torch, "float8_e4m3fn", None):
+        return t.view(torch.uint8)
+    raise TypeError("%s must hold E4M3 codes (uint8 or float8_e4m3fn), got %s" % (name, t.dtype))
+
+
+def chunk_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float, scale=None, out=None, lse=None,
+                  out_dtype=torch.bfloat16, workspace=None, stream=None):
+    """FP8 (E4M3) attention of every query row against one chunk of keys -> (O, LSE)."""
+    q, k, v = _e4m3(q, "q"), _e4m3(k, "k"), _e4m3(v, "v")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError("k, v must be [B, H, Skv, D] matching q")
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be contiguous fp32 [B, H, Sq]")
+    need = fp8_workspace_size(B, H, Skv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = load().attn_chunk_fwd_fp8(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),
+                                   _bhsd(v, "v"), float(q_descale), float(k_descale), float(v_descale), B, H, Sq,
+                                   Skv, D, _scale(scale, D), workspace.data_ptr(), workspace.numel(),
+                                   out.data_ptr(), _bhsd(out, "out"), _dt(out), lse.data_ptr(), _stream_ptr(stream))
+    _check(rc, "attn_chunk_fwd_fp8")
     return out, lse
 
 

@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "lse_merge.hip", "ulysses_relayout.hip", "attn_api.cpp"]
+SOURCES = ["attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_fwd_fp8.hip", "lse_merge.hip", "ulysses_relayout.hip",
+           "attn_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

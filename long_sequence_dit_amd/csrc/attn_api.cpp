@@ -360,6 +360,50 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
     return relayout(packed, x, xs, dt, B, H, S, D, n, false, (hipStream_t)stream);
 }
 
+size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Skv, int32_t D) {
+    if (B <= 0 || H <= 0 || Skv <= 0 || D != 128) return 0;
+    return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
+}
+
+attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                                 attn_strides_t vs, float q_descale, float k_descale, float v_descale, int32_t B,
+                                 int32_t H, int32_t Sq, int32_t Skv, int32_t D, float scale, void* workspace,
+                                 size_t ws_bytes, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                                 attn_stream_t stream) {
+    if (!valid_dtype(o_dt)) return ATTN_ERR_DTYPE;
+    if (D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return ATTN_ERR_SHAPE;
+    for (float x : {scale, q_descale, k_descale, v_descale})
+        if (!(x > 0.f) || !isfinite(x)) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * Sq == 0) return ATTN_OK;
+    if (!q || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+    if (!strides_ok(qs, 1) || !strides_ok(os, esize(o_dt))) return ATTN_ERR_ALIGN;
+    const hipStream_t s = (hipStream_t)stream;
+    if (Skv == 0)
+        return lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s) == hipSuccess
+                   ? ATTN_OK
+                   : ATTN_ERR_HIP;
+    if (!k || !v || !workspace) return ATTN_ERR_NULL;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
+    if (!strides_ok(ks, 1) || !strides_ok(vs, 1)) return ATTN_ERR_ALIGN;
+    // 32-bit buffer offsets: one head's K rows and V^T tiles, plus the tiles fetched past the end
+    if ((int64_t)(Skv + 256) * ks.s >= ((int64_t)1 << 31) || Skv >= (1 << 23)) return ATTN_ERR_UNSUPPORTED;
+    if (ws_bytes < attn_fp8_workspace_size(B, H, Skv, D)) return ATTN_ERR_WORKSPACE;
+    lsdit::Fp8Args a{};
+    a.q = q; a.k = k; a.v = v;
+    a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
+    a.vt = workspace;
+    a.o = o; a.os = S(os); a.o_bf16 = o_dt == ATTN_BF16;
+    a.lse = lse;
+    a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv;
+    a.c = (float)((double)scale * 1.4426950408889634 * (double)q_descale * (double)k_descale);
+    a.v_descale = v_descale;
+    if (!(a.c > 0.f) || !isfinite(a.c)) return ATTN_ERR_SHAPE;
+    if (lsdit::launch_fp8_pack_v(a, s) != hipSuccess) return ATTN_ERR_HIP;
+    return lsdit::launch_fwd_fp8(a, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 const char* attn_status_str(attn_status_t s) {
     switch (s) {
         case ATTN_OK: return "ok";

@@ -1,0 +1,556 @@
+// Chunk attention forward, FP8 (OCP E4M3) inputs, fp32 accumulation, gfx950 MFMA (D = 128).
+//
+// The computation of the bf16 kernel — O = softmax(scale * Q K^T) V for one chunk of keys and
+// the per-row natural-log LSE, blockwise over key tiles with an online softmax (NVIDIA
+// Technical Blog "Scaling AI Inference Across Multiple GPUs Using NVIDIA TensorRT with
+// Multi-Device Inference Support", section "Ring Attention") — on E4M3 tensors, the 8-bit
+// float format that suits attention layers ("TensorRT Multi-Device Inference: Engineering
+// Practices for Breaking Through Single-GPU Memory Bottlenecks", section "Why a Single GPU Is
+// No Longer Enough").  Each tensor holds E4M3 codes; its values are the codes times a
+// per-tensor descale.
+//
+// Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales): 64-deep
+// contractions at twice the bf16 MFMA rate, with half the bytes per operand.
+//  * S^T = K Q^T as in the bf16 kernel: 8 waves x 32 query rows, Q (B operand, 2 x 32 bytes
+//    per lane) in VGPRs, K tiles of 64 keys (8 KiB) from LDS, each lane ends with 32 scores of
+//    one query row.  The MFMA contracts A and B over the same (lane half, byte) positions, so
+//    any assignment of d to those positions works if Q and K use the same one: lane half h
+//    takes bytes 32h..32h+31 of each 64-wide d step.
+//  * P^T (E4M3) is the B operand of O^T += V^T P^T.  A lane's 32 probabilities, in register
+//    order, are its B bytes, which fixes which key each (lane half, byte) position stands for;
+//    V^T must present the same keys in the same positions.  A pre-pass (fp8_pack_v) writes V
+//    as such V^T tiles (128 rows of d x 64 key bytes, already in the LDS layout), so every
+//    operand read is a plain 16-byte LDS read and every tile load is one contiguous 8 KiB.
+//  * The row sum is one more MFMA per tile: an all-ones A operand times P^T puts the sum of
+//    the E4M3 probabilities of each query row (the values P.V uses) in every accumulator
+//    element of that row's lanes.
+//  * Probabilities are stored as E4M3(2^5 p): with the lazy rescale threshold 2^3, 2^5 p stays
+//    <= 256 (E4M3 tops out at 448), and probabilities down to 2^-11 of the reference are
+//    normal numbers; the 2^5 cancels in O = sum(P V) / sum(P) and is taken out of the LSE.
+//  * Descales fold into the kernel's constants: scale * log2(e) * q_descale * k_descale
+//    multiplies the scores, v_descale / l the output.
+// Loads, LDS swizzles, the tile ring and the loop barrier follow the bf16 kernel.
+#include "kernels.h"
+
+#include <math.h>
+#include <stddef.h>
+
+namespace lsdit {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+constexpr int D = 128;
+constexpr int NW = 8;               // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int BQ = 32 * NW;         // query rows per workgroup
+constexpr int BK = 64;              // keys per tile
+constexpr int K_ROW = D;            // bytes per K row
+constexpr int TILE = kFp8TileBytes; // bytes of a K tile and of a V^T tile
+constexpr int NSTAGE = 3;           // LDS buffers per tensor
+constexpr int LDS_BYTES = 2 * NSTAGE * TILE;
+constexpr int BLKS = TILE / 1024;   // wave-wide 1 KiB loads per tile
+constexpr int LOADERS = NW / 2;     // waves 0-3 issue the tile loads (as in the bf16 kernel)
+constexpr int BLKS_PER_WAVE = BLKS / LOADERS;
+static_assert(BLKS % LOADERS == 0, "tile must split evenly over the loading waves");
+constexpr float kRescale = 3.0f;    // lazy-rescale threshold, log2 units
+constexpr float kPShift = 5.0f;     // probabilities are stored as E4M3(2^kPShift * p)
+constexpr unsigned kOnes = 0x38383838u;  // four E4M3 ones
+constexpr int kUnitScale = 127;     // E8M0 block scale 2^0
+constexpr float kLn2 = 0.69314718055994531f;
+
+// Stream slots: P.V for d blocks 0..3, the row sum, then scores (kk, kb) with kb fastest.
+constexpr int N_PV = 5;
+constexpr int N_S = 4;
+constexpr int N_SLOTS = N_PV + N_S;
+constexpr int kPrefetch = 2;        // operands read this many slots ahead
+
+__device__ __forceinline__ f32x16_t mfma(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+    constexpr int X = 8;
+    const int q = n / X, r = n % X;
+    const int xcd = bid % X, slot = bid / X;
+    return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void half_pair(float x, float& a, float& b) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, v);
+}
+
+struct Rsrc {
+    i32x4_t w;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
+    const unsigned long long a = (unsigned long long)base;
+    Rsrc r;
+    r.w[0] = (int)(unsigned)a;
+    r.w[1] = (int)((unsigned)(a >> 32) & 0xFFFFu);
+    r.w[2] = num_records;
+    r.w[3] = 0x00020000;
+    return r;
+}
+
+// Wave-wide 16-byte-per-lane loads into consecutive 1 KiB LDS blocks (see the bf16 kernel for
+// why these are assembly: the kernel orders the LDS writes itself, by a vmcnt wait and the
+// loop barrier).
+template <int NB>
+__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB], int soff) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+        asm volatile(
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %0, %1, %2 offen lds"
+            :
+            : "v"(goff[i]), "s"(rs.w), "s"(soff), "{m0}"(dst + i * 1024u)
+            : "memory");
+}
+
+// K tile rows (128 bytes) in LDS: 16-byte chunk c of row r sits at position c ^ (r & 7), so
+// the 8 lanes of one LDS cycle (8 consecutive rows, same chunk) hit 8 distinct bank groups.
+__device__ __forceinline__ int k_swz(int row) { return row & 7; }
+// V^T tile rows (64 bytes, one per d): chunk c of row d at position c ^ ((d >> 2) & 3).
+__device__ __forceinline__ int vt_swz(int d) { return (d >> 2) & 3; }
+
+// Key held at byte position (lane half h, byte b) of a P^T / V^T operand: byte b of a lane's
+// probabilities is score f = b of that lane, i.e. accumulator element e = b & 15 of key block
+// kb = b >> 4, which is key 32 kb + 8 (e >> 2) + 4 h + (e & 3).
+__host__ __device__ constexpr int vt_key(int h, int b) {
+    return 32 * (b >> 4) + 8 * ((b & 15) >> 2) + 4 * h + (b & 3);
+}
+
+// ---- V^T pre-pass: one workgroup per (b, h, key tile).  Reads 64 rows of V (zeros past Skv)
+// and writes the 8 KiB V^T tile in the LDS layout the forward kernel loads verbatim:
+// row d (64 bytes) holds at byte 32h + b the value of key vt_key(h, b), chunk-swizzled.
+constexpr int PACK_T = 256;
+
+__global__ __launch_bounds__(PACK_T) void fp8_pack_v_kernel(Fp8Args a, int n_kt) {
+    __shared__ __attribute__((aligned(16))) unsigned char tile[BK * D];
+    const int g = blockIdx.x % n_kt, bh = blockIdx.x / n_kt;
+    const int b = bh / a.H, h = bh % a.H;
+    const unsigned char* vp = (const unsigned char*)a.v + b * a.vs.b + h * a.vs.h;
+    for (int i = threadIdx.x; i < BK * D / 16; i += PACK_T) {
+        const int r = i / (D / 16), c = i % (D / 16);
+        const int key = g * BK + r;
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (key < a.Skv) x = *(const u32x4_t*)(vp + (int64_t)key * a.vs.s + 16 * c);
+        *(u32x4_t*)(tile + r * D + 16 * c) = x;
+    }
+    __syncthreads();
+    unsigned char* out = (unsigned char*)a.vt + ((int64_t)bh * n_kt + g) * TILE;
+    for (int i = threadIdx.x; i < TILE / 16; i += PACK_T) {
+        const int d = i / 4, pos = i % 4;
+        const int c = pos ^ vt_swz(d);  // logical chunk stored at this position
+        const int hh = c >> 1, b0 = 16 * (c & 1);
+        unsigned w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            unsigned x = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x |= (unsigned)tile[vt_key(hh, b0 + 4 * j + u) * D + d] << (8 * u);
+            w[j] = x;
+        }
+        *(u32x4_t*)(out + 16 * i) = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// ---- forward kernel
+
+struct Wave {
+    f32x16_t acc[D / 32];  // O^T accumulators
+    f32x16_t lacc;         // row sums (every element of a lane: its row's sum)
+    i32x8_t qf[D / 64];    // Q bytes, B operands of the score MFMAs
+    float m_run;           // reference max (scaled, log2 domain)
+    float c;               // scale * log2(e) * q_descale * k_descale
+};
+
+struct Soft {
+    float mt[11];
+    float m_new, alpha, nb;  // nb = kPShift - m_new
+    float x[16][2];
+    float e[16][2];
+};
+
+__device__ __forceinline__ float sel_f(const f32x16_t (&s)[2], int f) { return s[f >> 4][f & 15]; }
+
+__device__ __forceinline__ void pin(float& a, float& b) { asm volatile("" : "+v"(a), "+v"(b)); }
+
+// Softmax schedule over the 9 slots of a stream: the max tree in slots 0-2, the reference
+// update in slot 3, then pair J of scores (2J, 2J+1) as a three-stage pipeline (FMA at a(J),
+// exp at a(J)+1, E4M3 pack at a(J)+2) with a(J) in 4..6.
+__host__ __device__ constexpr int pair_slot(int j) { return 4 + j / 6; }
+
+template <int POS, int J = 0>
+__device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&s)[2], i32x8_t& p) {
+    if constexpr (J < 16) {
+        constexpr int a = pair_slot(J);
+        if constexpr (POS == a) {
+            const float x0 = s[J >> 3][2 * (J & 7)], x1 = s[J >> 3][2 * (J & 7) + 1];
+            sm.x[J][0] = __builtin_fmaf(x0, c, sm.nb);
+            sm.x[J][1] = __builtin_fmaf(x1, c, sm.nb);
+            pin(sm.x[J][0], sm.x[J][1]);
+        } else if constexpr (POS == a + 1) {
+            sm.e[J][0] = fast_exp2(sm.x[J][0]);
+            sm.e[J][1] = fast_exp2(sm.x[J][1]);
+            pin(sm.e[J][0], sm.e[J][1]);
+        } else if constexpr (POS == a + 2) {
+            // bytes 2J, 2J+1 of the operand: half (J & 1) of dword J / 2
+            const unsigned old = (J & 1) ? (unsigned)p[J >> 1] : 0u;
+            p[J >> 1] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(sm.e[J][0], sm.e[J][1], old, (J & 1) != 0);
+        }
+        pair_stages<POS, J + 1>(c, sm, s, p);
+    }
+}
+
+template <int POS>
+__device__ __forceinline__ void softmax_slot(Wave& w, Soft& sm, const f32x16_t (&s)[2], i32x8_t& p) {
+    if constexpr (POS == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
+    } else if constexpr (POS == 1) {
+#pragma unroll
+        for (int i = 4; i < 8; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
+    } else if constexpr (POS == 2) {
+        sm.mt[8] = max3(sel_f(s, 24), sel_f(s, 25), sel_f(s, 26));
+        sm.mt[9] = max3(sel_f(s, 27), sel_f(s, 28), sel_f(s, 29));
+        sm.mt[10] = max3(sel_f(s, 30), sel_f(s, 31), sm.mt[0]);
+        sm.mt[1] = max3(sm.mt[1], sm.mt[2], sm.mt[3]);
+    } else if constexpr (POS == 3) {
+        const float mx = max3(max3(sm.mt[1], sm.mt[4], sm.mt[5]), max3(sm.mt[6], sm.mt[7], sm.mt[8]),
+                              fmaxf(sm.mt[9], sm.mt[10]));
+        float m0, m1;
+        half_pair(mx, m0, m1);
+        // lazy rescale: the reference moves only when the row max exceeds it by > kRescale,
+        // so p <= 2^kRescale and 2^kPShift p fits E4M3; lanes l and l+32 agree
+        const float m_tile = __builtin_amdgcn_fmed3f(m0, m1, INFINITY) * w.c;
+        sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
+        sm.alpha = fast_exp2(w.m_run - sm.m_new);
+        w.m_run = sm.m_new;
+        sm.nb = kPShift - sm.m_new;
+    }
+    pair_stages<POS>(w.c, sm, s, p);
+}
+
+template <int POS = 0>
+__device__ __forceinline__ void softmax_all(Wave& w, Soft& sm, const f32x16_t (&s)[2], i32x8_t& p) {
+    if constexpr (POS < N_SLOTS) {
+        softmax_slot<POS>(w, sm, s, p);
+        softmax_all<POS + 1>(w, sm, s, p);
+    }
+}
+
+// Per-lane LDS read offsets (bytes, buffer 0): V^T operand of d block dt at va[j] + 2048 dt,
+// K operand of (kk, kb) at ka[kk][j] + 4096 kb; j picks the operand's two 16-byte halves.
+struct Addr {
+    unsigned va[2];
+    unsigned ka[2][2];
+};
+
+// The 32-byte operand of slot SLOT (V^T / K); vb / kb_ carry the buffer offsets.
+template <int SLOT>
+__device__ __forceinline__ i32x8_t read_opnd(const Addr& ad, unsigned vb, unsigned kb_) {
+    u32x4_t lo, hi;
+    if constexpr (SLOT < 4) {
+        lo = *(const lds_u32x4_t*)(size_t)(ad.va[0] + vb + 2048u * SLOT);
+        hi = *(const lds_u32x4_t*)(size_t)(ad.va[1] + vb + 2048u * SLOT);
+    } else {
+        constexpr int sl = SLOT - N_PV, kk = sl >> 1, kb = sl & 1;
+        lo = *(const lds_u32x4_t*)(size_t)(ad.ka[kk][0] + kb_ + 4096u * kb);
+        hi = *(const lds_u32x4_t*)(size_t)(ad.ka[kk][1] + kb_ + 4096u * kb);
+    }
+    return i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Slots that read an operand: every slot but the row sum.
+__host__ __device__ constexpr bool reads(int slot) { return slot != 4; }
+// Index of slot's operand in the read sequence (the row-sum slot reads nothing).
+__host__ __device__ constexpr int read_idx(int slot) { return slot < 4 ? slot : slot - 1; }
+
+template <bool DO_PV, bool DO_S, bool DO_SM, int SLOT>
+__device__ __forceinline__ void stream_slots(Wave& w, const Addr& ad, unsigned vb, unsigned kb_,
+                                             i32x8_t (&ring)[kPrefetch], const i32x8_t& p_prev,
+                                             const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], i32x8_t& p_cur,
+                                             Soft& sm) {
+    constexpr int first = DO_PV ? 0 : N_PV;
+    constexpr int last = DO_S ? N_SLOTS : N_PV;
+    if constexpr (SLOT < last) {
+        if constexpr (SLOT < 4) {
+            w.acc[SLOT] = mfma(ring[read_idx(SLOT) % kPrefetch], p_prev, w.acc[SLOT]);
+        } else if constexpr (SLOT == 4) {
+            const i32x8_t ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes,
+                                  (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
+            w.lacc = mfma(ones, p_prev, w.lacc);
+        } else {
+            constexpr int sl = SLOT - N_PV, kk = sl >> 1, kb = sl & 1;
+            if constexpr (kk == 0) {
+                const f32x16_t zero = {};
+                s[kb] = mfma(ring[read_idx(SLOT) % kPrefetch], w.qf[kk], zero);
+            } else {
+                s[kb] = mfma(ring[read_idx(SLOT) % kPrefetch], w.qf[kk], s[kb]);
+            }
+        }
+        // read the operand kPrefetch reads ahead (the slot that consumes it)
+        if constexpr (reads(SLOT)) {
+            constexpr int nxt = read_idx(SLOT) + kPrefetch;                 // read index
+            constexpr int nslot = nxt < 4 ? nxt : nxt + 1;                  // its slot
+            if constexpr (nslot < last) ring[nxt % kPrefetch] = read_opnd<nslot>(ad, vb, kb_);
+        }
+        if constexpr (DO_SM) softmax_slot<SLOT>(w, sm, s_cur, p_cur);
+        __builtin_amdgcn_sched_barrier(0);
+        stream_slots<DO_PV, DO_S, DO_SM, SLOT + 1>(w, ad, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
+    }
+}
+
+// One stream: P.V (and row sum) of the tile at v0 with probabilities p_prev (if DO_PV), the
+// softmax of s_cur into p_cur (if DO_SM), the scores of the tile at k0 into s (if DO_S).
+template <bool DO_PV, bool DO_S, bool DO_SM>
+__device__ __forceinline__ void stream(Wave& w, const Addr& ad, unsigned v0, unsigned k0, const i32x8_t& p_prev,
+                                       const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], i32x8_t& p_cur, Soft& sm) {
+    static_assert(!DO_SM || (DO_PV && DO_S), "the softmax runs over a full stream");
+    constexpr int first = DO_PV ? 0 : N_PV;
+    static_assert(kPrefetch == 2, "the stream's first reads below assume two in flight");
+    i32x8_t ring[kPrefetch];
+    // the stream's first kPrefetch reads
+    if constexpr (first == 0) {
+        ring[0] = read_opnd<0>(ad, v0, k0);
+        ring[1] = read_opnd<1>(ad, v0, k0);
+    } else {
+        // score-only stream: reads are indexed from the first score slot
+        ring[read_idx(N_PV) % kPrefetch] = read_opnd<N_PV>(ad, v0, k0);
+        ring[read_idx(N_PV + 1) % kPrefetch] = read_opnd<N_PV + 1>(ad, v0, k0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    stream_slots<DO_PV, DO_S, DO_SM, first>(w, ad, v0, k0, ring, p_prev, s_cur, s, p_cur, sm);
+}
+
+__global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int n_kt) {
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    (void)smem;  // no static LDS: the dynamic block starts at LDS address 0
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hi = lane >> 5;
+    const int gidx = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = gidx / n_qt, qt = gidx % n_qt;
+    const int b = bh / a.H, h = bh % a.H;
+
+    const unsigned char* qp = (const unsigned char*)a.q + b * a.qs.b + h * a.qs.h;
+    const unsigned char* kp = (const unsigned char*)a.k + b * a.ks.b + h * a.ks.h;
+    const int Skv = a.Skv;
+    const int nkt = n_kt;
+
+    Wave w;
+    w.c = a.c;
+    w.m_run = -INFINITY;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) w.lacc[r] = 0.f;
+
+    // Q bytes: lane (row, half h) holds d = 64 kk + 32 h .. +32 of its row
+    const int qrow = qt * BQ + wave * 32 + (lane & 31);
+    const int qrow_c = qrow < a.Sq ? qrow : a.Sq - 1;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) {
+        const u32x4_t* src = (const u32x4_t*)(qp + (int64_t)qrow_c * a.qs.s + 64 * kk + 32 * hi);
+        const u32x4_t lo = src[0], hi4 = src[1];
+        w.qf[kk] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+    }
+
+    // tile loads: K rows through a per-lane swizzled offset, V^T tiles verbatim
+    const int k_rs = (int)a.ks.s;  // bytes per K row step
+    const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D);
+    const Rsrc vrs = make_rsrc((const unsigned char*)a.vt + (int64_t)bh * nkt * TILE, nkt * TILE);
+    int k_goff[BLKS_PER_WAVE], v_goff[BLKS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+        const int blk = wave * BLKS_PER_WAVE + i;
+        const int row = blk * 8 + lane / 8, slot = lane % 8;
+        k_goff[i] = row * k_rs + (slot ^ k_swz(row)) * 16;
+        v_goff[i] = blk * 1024 + lane * 16;
+    }
+    auto kbuf = [&](int t) { return (unsigned)((t % NSTAGE) * TILE); };
+    auto vbuf = [&](int t) { return (unsigned)((NSTAGE + t % NSTAGE) * TILE); };
+    auto load_k = [&](int g) {
+        if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(krs, kbuf(g) + wave * BLKS_PER_WAVE * 1024, k_goff, g * BK * k_rs);
+    };
+    auto load_v = [&](int g) {
+        if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(vrs, vbuf(g) + wave * BLKS_PER_WAVE * 1024, v_goff, g * TILE);
+    };
+
+    // per-lane operand offsets
+    Addr ad;
+    {
+        const int l32 = lane & 31;
+        ad.va[0] = l32 * 64 + (((2 * hi) ^ vt_swz(l32)) * 16);
+        ad.va[1] = l32 * 64 + (((2 * hi + 1) ^ vt_swz(l32)) * 16);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ad.ka[kk][j] = l32 * K_ROW + (((4 * kk + 2 * hi + j) ^ k_swz(l32)) * 16);
+    }
+
+    // scores of keys at or past `valid` in a tile -> -inf (key of element (kb, r) is
+    // 32 kb + 8 (r >> 2) + 4 hi + (r & 3))
+    auto mask = [&](f32x16_t(&s)[2], int valid) {
+        if (valid < BK) {
+            const int lim = valid - 4 * hi;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+        }
+    };
+    auto valid_of = [&](int t) { return Skv - t * BK; };
+
+    // prologue: zero the buffers (rows past the end are masked; zeros keep 0 * V finite)
+    for (int i = tid; i < LDS_BYTES / 16; i += NT) *(lds_u32x4_t*)(size_t)(16u * i) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < NSTAGE; ++g) load_k(g);
+#pragma unroll
+    for (int g = 0; g < NSTAGE - 2; ++g) load_v(g);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    f32x16_t sA[2], sB[2];
+    i32x8_t pA = {}, pB = {};
+    Soft sm;
+    auto finish_softmax = [&]() {
+        if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
+            // only element 0 of the row sums is read; the others may drift
+            w.lacc[0] *= sm.alpha;
+        }
+    };
+    stream<false, true, false>(w, ad, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
+    mask(sA, valid_of(0));
+    softmax_all(w, sm, sA, pA);  // P_0 -> pA
+    finish_softmax();
+    __syncthreads();
+
+    constexpr int kWaitPrev = 0x0F70 | ((NSTAGE - 2) * 2 * BLKS_PER_WAVE);
+    static_assert((NSTAGE - 2) * 2 * BLKS_PER_WAVE < 16, "vmcnt field");
+    auto iter = [&](int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2], f32x16_t(&s_next)[2]) {
+        load_k(t + NSTAGE);
+        load_v(t + NSTAGE - 2);
+        if (t == 0) {
+            stream<false, true, false>(w, ad, vbuf(0), kbuf(1), p_prev, s_cur, s_next, p_cur, sm);
+        } else {
+            stream<true, true, true>(w, ad, vbuf(t - 1), kbuf(t + 1), p_prev, s_cur, s_next, p_cur, sm);
+            finish_softmax();
+        }
+        if (t + 1 < nkt) mask(s_next, valid_of(t + 1));
+        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+        __syncthreads();
+    };
+    iter(0, pB, pA, sA, sB);
+    int t = 1;
+    for (; t + 1 < nkt; t += 2) {
+        iter(t, pA, pB, sB, sA);
+        iter(t + 1, pB, pA, sA, sB);
+    }
+    if (t < nkt) {
+        iter(t, pA, pB, sB, sA);
+        ++t;
+    }
+    if (nkt & 1)
+        stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
+    else
+        stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
+
+    // epilogue: O = acc * v_descale / l, LSE = ln2 (m + log2 l - kPShift)
+    const float l_tot = w.lacc[0];
+    const float inv_l = a.v_descale / l_tot;
+    const float lse2 = w.m_run + log2f(l_tot) - kPShift;
+    if (qrow < a.Sq) {
+        if (a.o_bf16) {
+            unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = 32 * dt + 8 * r4 + 4 * hi;
+                    u32x2_t wd;
+                    wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
+                    wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
+                    *(u32x2_t*)(op + d) = wd;
+                }
+        } else {
+            float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int d = 32 * dt + 8 * r4 + 4 * hi;
+                    *(u32x4_t*)(op + d) = u32x4_t{__float_as_uint(w.acc[dt][4 * r4] * inv_l),
+                                                  __float_as_uint(w.acc[dt][4 * r4 + 1] * inv_l),
+                                                  __float_as_uint(w.acc[dt][4 * r4 + 2] * inv_l),
+                                                  __float_as_uint(w.acc[dt][4 * r4 + 3] * inv_l)};
+                }
+        }
+        if (hi == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + qrow] = lse2 * kLn2;
+    }
+}
+
+}  // namespace
+
+int fp8_key_tiles(int Skv) { return (Skv + BK - 1) / BK; }
+
+hipError_t launch_fp8_pack_v(const Fp8Args& a, hipStream_t stream) {
+    const int n_kt = fp8_key_tiles(a.Skv);
+    const int64_t blocks = (int64_t)a.B * a.H * n_kt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_pack_v_kernel, dim3((unsigned)blocks), dim3(PACK_T), 0, stream, a, n_kt);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
+    const int n_qt = (a.Sq + BQ - 1) / BQ;
+    const int n_kt = fp8_key_tiles(a.Skv);
+    const int64_t blocks = (int64_t)a.B * a.H * n_qt;
+    if (blocks <= 0 || n_kt <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    static bool attr_set[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        e = hipFuncSetAttribute((const void*)fwd_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, stream, a, n_qt, n_kt);
+    return hipGetLastError();
+}
+
+}  // namespace lsdit

@@ -62,10 +62,33 @@ struct RelayoutArgs {
     int esize;           // bytes per element (2 or 4)
 };
 
+// FP8 (OCP E4M3) attention over one chunk of keys, D = 128.  q, k, v hold E4M3 codes (one
+// byte per element; strides in elements, i.e. bytes); their values are the codes times
+// per-tensor descales.  vt: V^T tiles written by launch_fp8_pack_v, kFp8TileBytes per
+// (b, h, 64-key tile), tile-major per head.
+constexpr int kFp8TileBytes = 8192;
+struct Fp8Args {
+    const void* q;
+    const void* k;
+    const void* v;
+    Strides qs, ks, vs;
+    void* vt;
+    void* o;             // [B, H, Sq, 128], o_bf16 ? bf16 : fp32, strides os
+    Strides os;
+    int o_bf16;
+    float* lse;          // [B, H, Sq] fp32 contiguous, natural log
+    int B, H, Sq, Skv;   // Skv >= 1
+    float c;             // scale * log2(e) * q_descale * k_descale
+    float v_descale;
+};
+int fp8_key_tiles(int Skv);
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_fp8_pack_v(const Fp8Args& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 // O = 0 and LSE = -inf for every row (a chunk without keys).
 // pack: src strided -> dst packed; unpack: src packed -> dst strided.
 hipError_t launch_ulysses_relayout(const RelayoutArgs& a, bool pack, hipStream_t stream);

@@ -113,6 +113,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 E4M3_MAX = 448.0
+_BLOCK = 1 << 20
 
 
 def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
@@ -129,6 +130,13 @@ def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     >= -6 and q = round-half-even(|x| / 2^(e-3)), the code is 8 (e + 6) + q
     (a q of 16 carries into the next binade by the same formula).
     """
+    x = np.asarray(x)
+    if x.size > _BLOCK:  # elementwise: encode in blocks (large temporaries are slow to allocate)
+        flat = x.reshape(-1)
+        out = np.empty(flat.shape, dtype=np.uint8)
+        for i in range(0, flat.size, _BLOCK):
+            out[i:i + _BLOCK] = f64_to_e4m3_bits(flat[i:i + _BLOCK])
+        return out.reshape(x.shape)
     x = np.asarray(x, dtype=np.float64)
     if not np.all(np.isfinite(x)):
         raise ValueError("E4M3 encoding of a non-finite value")
@@ -146,12 +154,17 @@ def f64_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
 def e4m3_quantize(x: np.ndarray):
     """Per-tensor E4M3 quantization: (codes, descale) with x ~= decode(codes) * descale.
 
-    descale = max|x| / 448 in fp32, so the largest magnitude maps to 448.
+    descale = max|x| / 448 in fp32, so the largest magnitude maps to 448; each element is
+    divided by it in fp64 and rounded once.
     """
-    x = np.asarray(x, dtype=np.float64)
-    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    x = np.asarray(x)
+    amax = float(max(np.max(x), -np.min(x))) if x.size else 0.0
     descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
-    return f64_to_e4m3_bits(x / descale), descale
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i in range(0, flat.size, _BLOCK):
+        out[i:i + _BLOCK] = f64_to_e4m3_bits(flat[i:i + _BLOCK].astype(np.float64) / descale)
+    return out.reshape(x.shape), descale
 
 
 def outlier_rows(seed: int, S: int, count: int) -> np.ndarray:

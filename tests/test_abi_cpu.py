@@ -30,7 +30,7 @@ def attn():
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src))
+    return set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src))
 
 
 def test_exports_every_declared_symbol(attn):
@@ -178,3 +178,32 @@ def test_ulysses_relayout_argument_errors(attn):
     assert pack(x=None, out=None, S=0) == OK and pack(x=None, out=None, B=0) == OK
     assert unpack(dt=9) == DTYPE and unpack(n=3) == SHAPE
     assert unpack(inp=None) == NULL and unpack(x=P + 8) == ALIGN
+
+
+def test_fp8_argument_errors(attn):
+    lib = attn.load()
+    c = _st(2 * 1000 * 128, 1000 * 128, 128)
+    need = lib.attn_fp8_workspace_size(1, 2, 20, 128)
+    assert need == 1 * 2 * 1 * 8192
+    assert lib.attn_fp8_workspace_size(1, 2, 65, 128) == 2 * 2 * 8192
+    assert lib.attn_fp8_workspace_size(1, 2, 20, 64) == 0 and lib.attn_fp8_workspace_size(1, 2, 0, 128) == 0
+
+    def f(q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=need, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1, dq=1.0, dk=1.0,
+          dv=1.0, odt=BF16, qs=None, ks=None, vs=None, os_=None):
+        return lib.attn_chunk_fwd_fp8(q, qs or c, k, ks or c, v, vs or c, dq, dk, dv, B, H, Sq, Skv, D, scale, ws,
+                                      ws_bytes, o, os_ or c, odt, lse, None)
+
+    assert f(odt=7) == DTYPE
+    assert f(D=64) == UNSUP
+    assert f(Sq=-1) == SHAPE and f(Skv=-2) == SHAPE
+    assert f(scale=0.0) == SHAPE and f(dq=float("nan")) == SHAPE and f(dv=-1.0) == SHAPE and f(dk=float("inf")) == SHAPE
+    assert f(q=None) == NULL and f(k=None) == NULL and f(ws=None) == NULL
+    assert f(q=P + 8) == ALIGN and f(ws=P + 8) == ALIGN
+    assert f(qs=_st(0, 0, 136)) == ALIGN      # E4M3 strides: multiples of 16 bytes
+    assert f(os_=_st(0, 0, 132)) == ALIGN     # bf16 output: multiples of 8 elements
+    assert f(ws_bytes=need - 1) == WS
+    assert f(ks=_st(0, 0, 2 ** 24)) == UNSUP  # one head's K rows must span < 2 GiB
+    assert f(Skv=2 ** 23, ws_bytes=1 << 62) == UNSUP
+    # no-ops, even with NULL pointers
+    assert f(q=None, k=None, v=None, o=None, lse=None, ws=None, Sq=0) == OK
+    assert f(q=None, k=None, v=None, o=None, lse=None, ws=None, H=0) == OK

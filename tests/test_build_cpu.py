@@ -1,7 +1,8 @@
-"""Properties of the built bf16 kernel that its code relies on (CPU only: hipcc cross-compiles).
+"""Properties of the built bf16 and FP8 kernels that their code relies on (CPU only: hipcc
+cross-compiles).
 
-The kernel addresses LDS with plain byte addresses from 0, which holds because it declares no
-static LDS: its whole LDS is the dynamic block, which then starts at address 0.
+The kernels address LDS with plain byte addresses from 0, which holds because they declare no
+static LDS: their whole LDS is the dynamic block, which then starts at address 0.
 """
 import os
 import re
@@ -22,13 +23,15 @@ def _device_asm(tmp_path, src):
     return out.read_text()
 
 
-def test_bf16_kernel_has_no_static_lds(tmp_path):
-    asm = _device_asm(tmp_path, "attn_fwd_bf16.hip")
+@pytest.mark.parametrize("src,kernel,count", [("attn_fwd_bf16.hip", "fwd_bf16_kernel", 2),  # D = 64, 128
+                                              ("attn_fwd_fp8.hip", "fwd_fp8_kernel", 1)])
+def test_forward_kernels_have_no_static_lds(tmp_path, src, kernel, count):
+    asm = _device_asm(tmp_path, src)
     blocks = re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm, re.S)
-    names = [n for n, _ in blocks if "fwd_bf16_kernel" in n]
-    assert len(names) == 2, names  # D = 64 and D = 128
+    names = [n for n, _ in blocks if kernel in n]
+    assert len(names) == count, names
     for name, body in blocks:
-        if "fwd_bf16_kernel" in name:
+        if kernel in name:
             m = re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", body)
             assert m and int(m.group(1)) == 0, (name, m and m.group(0))
             assert re.search(r"\.amdhsa_private_segment_fixed_size 0\b", body), name  # no scratch either
