@@ -35,6 +35,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <type_traits>
+
 namespace lsdit {
 namespace {
 
@@ -53,7 +55,7 @@ constexpr int BQ = 32 * NW;         // query rows per workgroup
 constexpr int BK = 64;              // keys per tile
 constexpr int K_ROW = D;            // bytes per K row
 constexpr int TILE = kFp8TileBytes; // bytes of a K tile and of a V^T tile
-constexpr int NSTAGE = 3;           // LDS buffers per tensor
+constexpr int NSTAGE = 4;           // LDS buffers per tensor (the key loop is unrolled by NSTAGE)
 constexpr int LDS_BYTES = 2 * NSTAGE * TILE;
 constexpr int BLKS = TILE / 1024;   // wave-wide 1 KiB loads per tile
 constexpr int LOADERS = NW / 2;     // waves 0-3 issue the tile loads (as in the bf16 kernel)
@@ -181,6 +183,7 @@ struct Wave {
     f32x16_t acc[D / 32];  // O^T accumulators
     f32x16_t lacc;         // row sums (every element of a lane: its row's sum)
     i32x8_t qf[D / 64];    // Q bytes, B operands of the score MFMAs
+    i32x8_t ones;          // E4M3 ones, the A operand of the row-sum MFMA
     float m_run;           // reference max (scaled, log2 domain)
     float c;               // scale * log2(e) * q_descale * k_descale
 };
@@ -215,9 +218,10 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
             sm.e[J][1] = fast_exp2(sm.x[J][1]);
             pin(sm.e[J][0], sm.e[J][1]);
         } else if constexpr (POS == a + 2) {
-            // bytes 2J, 2J+1 of the operand: half (J & 1) of dword J / 2
-            const unsigned old = (J & 1) ? (unsigned)p[J >> 1] : 0u;
-            p[J >> 1] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(sm.e[J][0], sm.e[J][1], old, (J & 1) != 0);
+            // bytes 2J, 2J+1 of the operand: half (J & 1) of dword J / 2.  The conversion keeps
+            // the other half of the dword it is given; for the low half that is a stale value
+            // the high half's conversion then replaces (no zeroing needed)
+            p[J >> 1] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(sm.e[J][0], sm.e[J][1], (unsigned)p[J >> 1], (J & 1) != 0);
         }
         pair_stages<POS, J + 1>(c, sm, s, p);
     }
@@ -298,9 +302,7 @@ __device__ __forceinline__ void stream_slots(Wave& w, const Addr& ad, unsigned v
         if constexpr (SLOT < 4) {
             w.acc[SLOT] = mfma(ring[read_idx(SLOT) % kPrefetch], p_prev, w.acc[SLOT]);
         } else if constexpr (SLOT == 4) {
-            const i32x8_t ones = {(int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes,
-                                  (int)kOnes, (int)kOnes, (int)kOnes, (int)kOnes};
-            w.lacc = mfma(ones, p_prev, w.lacc);
+            w.lacc = mfma(w.ones, p_prev, w.lacc);
         } else {
             constexpr int sl = SLOT - N_PV, kk = sl >> 1, kb = sl & 1;
             if constexpr (kk == 0) {
@@ -369,6 +371,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) w.lacc[r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) w.ones[r] = (int)kOnes;
+    asm volatile("" : "+v"(w.ones));  // kept in registers, not rebuilt before every use
 
     // Q bytes: lane (row, half h) holds d = 64 kk + 32 h .. +32 of its row
     const int qrow = qt * BQ + wave * 32 + (lane & 31);
@@ -393,6 +398,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         k_goff[i] = row * k_rs + (slot ^ k_swz(row)) * 16;
         v_goff[i] = blk * 1024 + lane * 16;
     }
+    // LDS byte offsets of the tile buffers: tile g of K and V sits in buffer g mod NSTAGE
     auto kbuf = [&](int t) { return (unsigned)((t % NSTAGE) * TILE); };
     auto vbuf = [&](int t) { return (unsigned)((NSTAGE + t % NSTAGE) * TILE); };
     auto load_k = [&](int g) {
@@ -412,6 +418,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int j = 0; j < 2; ++j) ad.ka[kk][j] = l32 * K_ROW + (((4 * kk + 2 * hi + j) ^ k_swz(l32)) * 16);
+        // opaque to the compiler, so that buffer and block offsets stay additions it folds into
+        // the reads' offset fields (with the offsets' bits known disjoint it may turn them
+        // into ORs computed per read)
+        asm volatile("" : "+v"(ad.va[0]), "+v"(ad.va[1]), "+v"(ad.ka[0][0]), "+v"(ad.ka[0][1]), "+v"(ad.ka[1][0]),
+                     "+v"(ad.ka[1][1]));
     }
 
     // scores of keys at or past `valid` in a tile -> -inf (key of element (kb, r) is
@@ -459,27 +470,49 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
 
     constexpr int kWaitPrev = 0x0F70 | ((NSTAGE - 2) * 2 * BLKS_PER_WAVE);
     static_assert((NSTAGE - 2) * 2 * BLKS_PER_WAVE < 16, "vmcnt field");
-    auto iter = [&](int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2], f32x16_t(&s_next)[2]) {
+    // Iteration t, with P = t mod NSTAGE a compile-time constant: the buffers it reads are then
+    // constants, which fold into the LDS reads' offset fields.
+    auto iter = [&](auto phase, int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2],
+                    f32x16_t(&s_next)[2]) {
+        constexpr int P = decltype(phase)::value;
+        constexpr unsigned k_next = ((P + 1) % NSTAGE) * TILE;               // K_{t+1}
+        constexpr unsigned v_prev = (NSTAGE + (P + NSTAGE - 1) % NSTAGE) * TILE;  // V_{t-1}
         load_k(t + NSTAGE);
         load_v(t + NSTAGE - 2);
         if (t == 0) {
-            stream<false, true, false>(w, ad, vbuf(0), kbuf(1), p_prev, s_cur, s_next, p_cur, sm);
+            stream<false, true, false>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
         } else {
-            stream<true, true, true>(w, ad, vbuf(t - 1), kbuf(t + 1), p_prev, s_cur, s_next, p_cur, sm);
+            stream<true, true, true>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
             finish_softmax();
         }
         if (t + 1 < nkt) mask(s_next, valid_of(t + 1));
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
     };
-    iter(0, pB, pA, sA, sB);
+    static_assert(NSTAGE == 4, "the unrolled loop below walks four phases");
+    using Ph0 = std::integral_constant<int, 0>;
+    using Ph1 = std::integral_constant<int, 1>;
+    using Ph2 = std::integral_constant<int, 2>;
+    using Ph3 = std::integral_constant<int, 3>;
+    iter(Ph0{}, 0, pB, pA, sA, sB);
     int t = 1;
-    for (; t + 1 < nkt; t += 2) {
-        iter(t, pA, pB, sB, sA);
-        iter(t + 1, pB, pA, sA, sB);
+    for (; t + 3 < nkt; t += 4) {
+        iter(Ph1{}, t, pA, pB, sB, sA);
+        iter(Ph2{}, t + 1, pB, pA, sA, sB);
+        iter(Ph3{}, t + 2, pA, pB, sB, sA);
+        iter(Ph0{}, t + 3, pB, pA, sA, sB);
+    }
+    // t = 1 mod 4 here: at most three more iterations, of phases 1, 2, 3
+    if (t < nkt) {
+        iter(Ph1{}, t, pA, pB, sB, sA);
+        ++t;
     }
     if (t < nkt) {
-        iter(t, pA, pB, sB, sA);
+        iter(Ph2{}, t, pB, pA, sA, sB);
+        ++t;
+    }
+    if (t < nkt) {
+        iter(Ph3{}, t, pA, pB, sB, sA);
         ++t;
     }
     if (nkt & 1)
