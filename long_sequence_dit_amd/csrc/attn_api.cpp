@@ -387,8 +387,9 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     if (!k || !v || !workspace) return ATTN_ERR_NULL;
     if (!aligned16(k) || !aligned16(v) || !aligned16(workspace)) return ATTN_ERR_ALIGN;
     if (!strides_ok(ks, 1) || !strides_ok(vs, 1)) return ATTN_ERR_ALIGN;
-    // 32-bit buffer offsets: one head's K rows and V^T tiles, plus the tiles fetched past the end
-    if ((int64_t)(Skv + 256) * ks.s >= ((int64_t)1 << 31) || Skv >= (1 << 23)) return ATTN_ERR_UNSUPPORTED;
+    // 32-bit buffer offsets: one head's K rows and V^T tiles, plus the four tiles the kernel
+    // fetches past the end
+    if ((int64_t)(Skv + 320) * ks.s >= ((int64_t)1 << 31) || Skv >= (1 << 23)) return ATTN_ERR_UNSUPPORTED;
     if (ws_bytes < attn_fp8_workspace_size(B, H, Skv, D)) return ATTN_ERR_WORKSPACE;
     lsdit::Fp8Args a{};
     a.q = q; a.k = k; a.v = v;

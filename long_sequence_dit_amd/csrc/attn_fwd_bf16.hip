@@ -33,8 +33,10 @@
 //    MFMA (exposing the LDS latency on every MFMA) and bunches the MFMAs
 //    apart from the VALU;
 //  * K/V tiles of 64 rows go HBM -> LDS directly (buffer loads with the LDS
-//    destination) into three buffers each, K issued two iterations and V
-//    one iteration before use, through buffer resources whose out-of-range
+//    destination) into four buffers each (K in the low 64 KiB, V above), K
+//    issued three iterations and V two iterations before use, and the key
+//    loop is unrolled by four, so every LDS read names its buffer by a
+//    compile-time offset; loads go through buffer resources whose out-of-range
 //    rows read as zero (and are masked); waves 0-3 issue all of them (the
 //    older wave of each SIMD, which otherwise idles at the loop barrier);
 //    LDS rows are XOR swizzled in 16-byte chunks so both the row reads of K
@@ -49,6 +51,8 @@
 
 #include <math.h>
 #include <stddef.h>
+
+#include <type_traits>
 
 namespace lsdit {
 namespace {
@@ -83,7 +87,8 @@ struct Cfg {
     static constexpr int CH = D / 8;              // 16-byte chunks per row
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = BK * ROW_BYTES;
-    static constexpr int NSTAGE = 3;                        // LDS buffers per tensor
+    static constexpr int NSTAGE = 4;                        // LDS buffers per tensor (loop unrolled by NSTAGE)
+    static constexpr int V_REGION = NSTAGE * TILE_BYTES;    // K buffers below, V buffers from here
     static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;
     static constexpr int ROWS_PER_BLK = 64 / CH;            // rows one wave-wide 1 KiB load covers
     static constexpr int BLKS = BK / ROWS_PER_BLK;          // 1 KiB blocks per tile
@@ -228,7 +233,8 @@ struct Wave {
     bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
     float m_run;           // reference max (scaled, log2 domain)
     float l_run;           // this lane's share of the running row sum
-    unsigned k_base, v_base;  // per-lane LDS read addresses in buffer 0 (see the kernel)
+    unsigned k_lane[D / 16];  // per-lane LDS read address of K operand kk in K buffer 0
+    unsigned v_lane[D / 32];  // per-lane LDS read address of V^T operand dt in V buffer 0
     float c;               // scale * log2(e)
 };
 
@@ -341,20 +347,21 @@ __device__ __forceinline__ void softmax_all(Wave<D>& w, Soft& sm, const f32x16_t
 // are untouched); XOR-ing the slot constant into that loop-variant value keeps the compiler
 // from hoisting a table of loop-invariant addresses out of the key loop (and spilling it).
 template <int D, int SLOT>
-__device__ __forceinline__ u32x4_t read_opnd(unsigned vb, unsigned kb_) {
+__device__ __forceinline__ u32x4_t read_opnd(const Wave<D>& w, unsigned vb, unsigned kb_) {
     using C = Cfg<D>;
-    // vb and kb_ are LDS byte addresses, so each read's address is one XOR of a per-lane
-    // register with a constant, plus the instruction offset
+    // vb and kb_ are the buffers' byte offsets within the V and K regions: in the unrolled key
+    // loop compile-time constants, so each address is a per-lane register plus the read's
+    // offset field
     if constexpr (SLOT < C::N_PV) {
         constexpr int ks = SLOT / (D / 32), dt = SLOT % (D / 32);
-        const unsigned a = (vb ^ (dt << 6)) + 16 * ks * C::ROW_BYTES;
+        const unsigned a = w.v_lane[dt] + vb + 16 * ks * C::ROW_BYTES;
         const u32x2_t lo = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)a));
         const u32x2_t hi = __builtin_bit_cast(
             u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(size_t)(a + 8 * C::ROW_BYTES)));
         return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
     } else {
         constexpr int sl = SLOT - C::N_PV, kk = sl >> 1, kb = sl & 1;
-        return *(const lds_u32x4_t*)(size_t)((kb_ ^ (kk << 5)) + kb * 32 * C::ROW_BYTES);
+        return *(const lds_u32x4_t*)(size_t)(w.k_lane[kk] + kb_ + kb * 32 * C::ROW_BYTES);
     }
 }
 
@@ -385,7 +392,7 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned k
                                                                 0, 0);
             }
         }
-        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(vb, kb_);
+        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(w, vb, kb_);
         if constexpr (DO_SM && pos < last_a_slot<D>() + 3) softmax_slot<D, pos>(w, sm, s_cur, p_cur);
         __builtin_amdgcn_sched_barrier(0);
         stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
@@ -393,12 +400,13 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned k
 }
 
 template <int D, bool DO_PV, int I = 0>
-__device__ __forceinline__ void ring_fill(unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch], int last) {
+__device__ __forceinline__ void ring_fill(const Wave<D>& w, unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch],
+                                          int last) {
     using C = Cfg<D>;
     constexpr int first = DO_PV ? 0 : C::N_PV;
     if constexpr (I < kPrefetch) {
-        if (first + I < last) ring[I] = read_opnd<D, first + I>(vb, kb_);
-        ring_fill<D, DO_PV, I + 1>(vb, kb_, ring, last);
+        if (first + I < last) ring[I] = read_opnd<D, first + I>(w, vb, kb_);
+        ring_fill<D, DO_PV, I + 1>(w, vb, kb_, ring, last);
     }
 }
 
@@ -413,9 +421,9 @@ __device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, const u32x4_t
     static_assert(C::N_PV >= 8 && C::N_S >= 2, "stream too short for the softmax pipeline");
     constexpr int first = DO_PV ? 0 : C::N_PV;
     constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
-    const unsigned vb = w.v_base | v0, kb_ = w.k_base | k0;
+    const unsigned vb = v0, kb_ = k0;
     u32x4_t ring[kPrefetch];
-    ring_fill<D, DO_PV>(vb, kb_, ring, last);
+    ring_fill<D, DO_PV>(w, vb, kb_, ring, last);
     __builtin_amdgcn_sched_barrier(0);
     stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
 }
@@ -493,9 +501,10 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     // address: the block's address is a link-time constant the compiler cannot fold.)
     (void)smem;
     constexpr unsigned lds_base = 0;
-    // LDS byte offsets of the tile buffers (the dynamic LDS block starts at offset 0)
-    auto kbuf = [&](int t) { return (t % C::NSTAGE) * C::TILE_BYTES; };
-    auto vbuf = [&](int t) { return (C::NSTAGE + t % C::NSTAGE) * C::TILE_BYTES; };
+    // Offsets of tile t's buffers within the K region (LDS address 0) and the V region (LDS
+    // address V_REGION)
+    auto kbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
+    auto vbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
     // Three walks over the tile sequence: the next K tile to load (tile t + NSTAGE during
     // iteration t), the next V tile to load (tile t + NSTAGE - 2) and the next tile to mask
     // (tile t + 1).  Tile g of the sequence goes into buffer g mod NSTAGE.
@@ -510,7 +519,8 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     };
     auto load_v = [&](int g) {
         if (wave < C::LOADERS)
-            lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff, wv.row * v_rs);
+            lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + C::V_REGION + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff,
+                                      wv.row * v_rs);
         wv.next(n_chunks, v_row, v_len, Skv);
     };
     auto next_valid = [&]() {  // valid keys of the next tile to mask
@@ -519,21 +529,34 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         return valid;
     };
 
-    // ---- per-lane LDS read addresses in buffer 0 (bytes; a buffer ORs in a multiple of
-    // 16 KiB).  Each swizzle XOR only touches chunk-index bits that the loop index sets
-    // independently, so one per-lane address XOR-ed with a compile-time constant addresses
-    // every operand; row steps are additive.
+    // ---- per-lane LDS read addresses in buffer 0 of each region.  Each swizzle XOR only
+    // touches chunk-index bits that the operand index sets independently, so the operand
+    // index enters as an XOR with a constant (taken once here, one register per operand
+    // column) and row steps, key blocks and buffers as additions (folded into the reads'
+    // offset fields).
     // K operand (kb, kk): row kb*32 + (lane&31), chunk 2kk + hi  ->  k_base ^ (kk << 5)
     // (k_swz(row + 32) == k_swz(row)).
-    w.k_base = (lane & 31) * C::ROW_BYTES + ((hi ^ k_swz<D>(lane & 31)) * 16);
+    {
+        const unsigned k_base = (lane & 31) * C::ROW_BYTES + ((hi ^ k_swz<D>(lane & 31)) * 16);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) w.k_lane[kk] = k_base ^ (kk << 5);
+    }
     // V^T operand (dt, ks, lo/hi): rows 16ks + 4(g>>1) + (j>>2) (+8), element columns
     // 32dt + 16(g&1) + 4(j&3)  ->  v_base ^ (dt << 6); v_swz depends on row & 3 only.
     {
         const int g = lane >> 4, j = lane & 15;
         const int v_row0 = 4 * (g >> 1) + (j >> 2);
         const int v_col0 = 16 * (g & 1) + 4 * (j & 3);
-        w.v_base = v_row0 * C::ROW_BYTES + (((v_col0 >> 3) ^ v_swz<D>(v_row0)) * 16) + (v_col0 & 7) * 2;
+        const unsigned v_base = v_row0 * C::ROW_BYTES + (((v_col0 >> 3) ^ v_swz<D>(v_row0)) * 16) + (v_col0 & 7) * 2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) w.v_lane[dt] = C::V_REGION + (v_base ^ (dt << 6));
     }
+    // opaque to the compiler, so the offsets stay additions folded into the reads' offset
+    // fields (with their bits known disjoint it may turn them into ORs computed per read)
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(w.k_lane[kk]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(w.v_lane[dt]));
 
     // Key of accumulator element (kb, r) is kb*32 + 8(r>>2) + 4hi + (r&3); compare its
     // compile-time part against valid - 4hi, so no table of per-lane key indices is kept live.
@@ -583,7 +606,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     mask(sA, next_valid());
     softmax_all<D>(w, sm, sA, pA);  // P_0 -> pA
     finish_softmax();
-    __syncthreads();  // every wave is done with K buffer 0 before tile 3 overwrites it
+    __syncthreads();  // every wave is done with K buffer 0 before tile NSTAGE overwrites it
 
     // ---- key loop.  Iteration t: issue K_{t+NSTAGE} (into K_t's buffer) and V_{t+NSTAGE-2}
     // (into V_{t-2}'s buffer); stream P.V of tile t-1 with the softmax of tile t, then the
@@ -592,30 +615,55 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     // V_t in iteration t+1 (P.V), each before the barrier that precedes its buffer's refill.
     // Scores of tile nkt are computed from a stale buffer and never used.  The probability
     // registers swap roles every iteration (pA <-> pB), and so do the score registers.
-    // vmcnt(loads issued in the last NSTAGE - 2 iterations)
-    constexpr int kWaitPrev = 0x0F70 | ((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE);
-    static_assert((C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE < 16, "vmcnt field");
-    auto iter = [&](int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2], f32x16_t(&s_next)[2]) {
+    // vmcnt(loads issued in the last NSTAGE - 2 iterations); the counter's 6 bits are split
+    // into bits 3:0 and 15:14 of the wait's immediate
+    constexpr int kPrevLoads = (C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE;
+    static_assert(kPrevLoads < 64, "vmcnt field");
+    constexpr int kWaitPrev = 0x0F70 | (kPrevLoads & 15) | ((kPrevLoads >> 4) << 14);
+    // Iteration t, with P = t mod NSTAGE a compile-time constant: the buffers it reads are then
+    // constants, which fold into the LDS reads' offset fields.
+    auto iter = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
+                    f32x16_t(&s_next)[2]) {
+        constexpr int P = decltype(phase)::value;
+        constexpr unsigned k_next = ((P + 1) % C::NSTAGE) * C::TILE_BYTES;                // K_{t+1}
+        constexpr unsigned v_prev = ((P + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES;    // V_{t-1}
         load_k(t + C::NSTAGE);
         load_v(t + C::NSTAGE - 2);
         if (t == 0) {
-            stream<D, false, true, false>(w, vbuf(0), kbuf(1), p_prev, s_cur, s_next, p_cur, sm);
+            stream<D, false, true, false>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
         } else {
-            stream<D, true, true, true>(w, vbuf(t - 1), kbuf(t + 1), p_prev, s_cur, s_next, p_cur, sm);
+            stream<D, true, true, true>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
             finish_softmax();
         }
         if (t + 1 < nkt) mask(s_next, next_valid());
         __builtin_amdgcn_s_waitcnt(kWaitPrev);
         __syncthreads();
     };
-    iter(0, pB, pA, sA, sB);  // scores S_1 -> sB
+    static_assert(C::NSTAGE == 4, "the unrolled loop below walks four phases");
+    using Ph0 = std::integral_constant<int, 0>;
+    using Ph1 = std::integral_constant<int, 1>;
+    using Ph2 = std::integral_constant<int, 2>;
+    using Ph3 = std::integral_constant<int, 3>;
+    iter(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
     int t = 1;
-    for (; t + 1 < nkt; t += 2) {
-        iter(t, pA, pB, sB, sA);      // P.V with P_{t-1} = pA, softmax S_t (sB) -> pB, S_{t+1} -> sA
-        iter(t + 1, pB, pA, sA, sB);  // P.V with P_t = pB, softmax S_{t+1} (sA) -> pA, S_{t+2} -> sB
+    // odd t: P.V with P_{t-1} = pA, softmax S_t (sB) -> pB, S_{t+1} -> sA; even t: the reverse
+    for (; t + 3 < nkt; t += 4) {
+        iter(Ph1{}, t, pA, pB, sB, sA);
+        iter(Ph2{}, t + 1, pB, pA, sA, sB);
+        iter(Ph3{}, t + 2, pA, pB, sB, sA);
+        iter(Ph0{}, t + 3, pB, pA, sA, sB);
+    }
+    // t = 1 mod 4 here: at most three more iterations, of phases 1, 2, 3
+    if (t < nkt) {
+        iter(Ph1{}, t, pA, pB, sB, sA);
+        ++t;
     }
     if (t < nkt) {
-        iter(t, pA, pB, sB, sA);
+        iter(Ph2{}, t, pB, pA, sA, sB);
+        ++t;
+    }
+    if (t < nkt) {
+        iter(Ph3{}, t, pA, pB, sB, sA);
         ++t;
     }
     // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)

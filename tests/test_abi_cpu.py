@@ -203,6 +203,8 @@ def test_fp8_argument_errors(attn):
     assert f(os_=_st(0, 0, 132)) == ALIGN     # bf16 output: multiples of 8 elements
     assert f(ws_bytes=need - 1) == WS
     assert f(ks=_st(0, 0, 2 ** 24)) == UNSUP  # one head's K rows must span < 2 GiB
+    # ... including the four tiles fetched past the end: (200 + 320) * 2^22 >= 2^31 > (200 + 256) * 2^22
+    assert f(ks=_st(0, 0, 2 ** 22), Skv=200) == UNSUP
     assert f(Skv=2 ** 23, ws_bytes=1 << 62) == UNSUP
     # no-ops, even with NULL pointers
     assert f(q=None, k=None, v=None, o=None, lse=None, ws=None, Sq=0) == OK
