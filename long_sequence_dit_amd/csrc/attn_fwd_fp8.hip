@@ -442,10 +442,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
     // prologue: zero the buffers (rows past the end are masked; zeros keep 0 * V finite)
     for (int i = tid; i < LDS_BYTES / 16; i += NT) *(lds_u32x4_t*)(size_t)(16u * i) = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
+    // every K buffer, and the V tiles of the first pair of iterations (see below)
 #pragma unroll
     for (int g = 0; g < NSTAGE; ++g) load_k(g);
 #pragma unroll
-    for (int g = 0; g < NSTAGE - 2; ++g) load_v(g);
+    for (int g = 0; g < NSTAGE / 2; ++g) load_v(g);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
@@ -468,17 +469,15 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
     finish_softmax();
     __syncthreads();
 
-    constexpr int kWaitPrev = 0x0F70 | ((NSTAGE - 2) * 2 * BLKS_PER_WAVE);
-    static_assert((NSTAGE - 2) * 2 * BLKS_PER_WAVE < 16, "vmcnt field");
-    // Iteration t, with P = t mod NSTAGE a compile-time constant: the buffers it reads are then
+    // Iteration t: P.V of tile t-1 (V_{t-1}), the softmax of tile t, the scores of tile t+1
+    // (K_{t+1}).  With P = t mod NSTAGE a compile-time constant, the buffers it reads are
     // constants, which fold into the LDS reads' offset fields.
-    auto iter = [&](auto phase, int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2],
-                    f32x16_t(&s_next)[2]) {
+    // (always inlined: as calls, the register arrays they touch would go to scratch)
+    auto body = [&](auto phase, int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2],
+                    f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
         constexpr int P = decltype(phase)::value;
-        constexpr unsigned k_next = ((P + 1) % NSTAGE) * TILE;               // K_{t+1}
+        constexpr unsigned k_next = ((P + 1) % NSTAGE) * TILE;                     // K_{t+1}
         constexpr unsigned v_prev = (NSTAGE + (P + NSTAGE - 1) % NSTAGE) * TILE;  // V_{t-1}
-        load_k(t + NSTAGE);
-        load_v(t + NSTAGE - 2);
         if (t == 0) {
             stream<false, true, false>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
         } else {
@@ -486,34 +485,42 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             finish_softmax();
         }
         if (t + 1 < nkt) mask(s_next, valid_of(t + 1));
-        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+    };
+    // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
+    // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
+    // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
+    // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
+    // they wait for those loads, and the barrier publishes them.
+    static_assert(NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
+    auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
+        load_k(t + 3);
+        load_k(t + 4);
+        load_v(t + 1);
+        load_v(t + 2);
+        body(ph0, t, pA, pB, sB, sA);                 // odd t: P_{t-1} in pA, S_t in sB
+        if (t + 1 < nkt) body(ph1, t + 1, pB, pA, sA, sB);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
     };
-    static_assert(NSTAGE == 4, "the unrolled loop below walks four phases");
     using Ph0 = std::integral_constant<int, 0>;
     using Ph1 = std::integral_constant<int, 1>;
     using Ph2 = std::integral_constant<int, 2>;
     using Ph3 = std::integral_constant<int, 3>;
-    iter(Ph0{}, 0, pB, pA, sA, sB);
+    body(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
+    __syncthreads();                 // K_1's buffer is refilled by the first pair
     int t = 1;
     for (; t + 3 < nkt; t += 4) {
-        iter(Ph1{}, t, pA, pB, sB, sA);
-        iter(Ph2{}, t + 1, pB, pA, sA, sB);
-        iter(Ph3{}, t + 2, pA, pB, sB, sA);
-        iter(Ph0{}, t + 3, pB, pA, sA, sB);
+        pair(Ph1{}, Ph2{}, t);
+        pair(Ph3{}, Ph0{}, t + 2);
     }
-    // t = 1 mod 4 here: at most three more iterations, of phases 1, 2, 3
+    // t = 1 mod 4 here: at most three more iterations
     if (t < nkt) {
-        iter(Ph1{}, t, pA, pB, sB, sA);
-        ++t;
+        pair(Ph1{}, Ph2{}, t);
+        t += 2;
     }
     if (t < nkt) {
-        iter(Ph2{}, t, pB, pA, sA, sB);
-        ++t;
-    }
-    if (t < nkt) {
-        iter(Ph3{}, t, pA, pB, sB, sA);
-        ++t;
+        pair(Ph3{}, Ph0{}, t);
+        t += 2;
     }
     if (nkt & 1)
         stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
