@@ -581,7 +581,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 #pragma unroll
     for (int g = 0; g < C::NSTAGE; ++g) load_k(g);
 #pragma unroll
-    for (int g = 0; g < C::NSTAGE - 2; ++g) load_v(g);
+    for (int g = 0; g < C::NSTAGE / 2; ++g) load_v(g);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
     __syncthreads();
 
@@ -608,27 +608,18 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     finish_softmax();
     __syncthreads();  // every wave is done with K buffer 0 before tile NSTAGE overwrites it
 
-    // ---- key loop.  Iteration t: issue K_{t+NSTAGE} (into K_t's buffer) and V_{t+NSTAGE-2}
-    // (into V_{t-2}'s buffer); stream P.V of tile t-1 with the softmax of tile t, then the
-    // scores of tile t+1; then wait for the loads that iteration t+1 reads (K_{t+2}, V_t, both
-    // issued NSTAGE - 2 iterations ago) and sync.  K_t is read in iteration t-1 (scores) and
-    // V_t in iteration t+1 (P.V), each before the barrier that precedes its buffer's refill.
-    // Scores of tile nkt are computed from a stale buffer and never used.  The probability
-    // registers swap roles every iteration (pA <-> pB), and so do the score registers.
-    // vmcnt(loads issued in the last NSTAGE - 2 iterations); the counter's 6 bits are split
-    // into bits 3:0 and 15:14 of the wait's immediate
-    constexpr int kPrevLoads = (C::NSTAGE - 2) * 2 * C::BLKS_PER_WAVE;
-    static_assert(kPrevLoads < 64, "vmcnt field");
-    constexpr int kWaitPrev = 0x0F70 | (kPrevLoads & 15) | ((kPrevLoads >> 4) << 14);
-    // Iteration t, with P = t mod NSTAGE a compile-time constant: the buffers it reads are then
-    // constants, which fold into the LDS reads' offset fields.
-    auto iter = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
-                    f32x16_t(&s_next)[2]) {
+    // ---- key loop.  Iteration t streams P.V of tile t-1 (V_{t-1}) with the softmax of tile t,
+    // then the scores of tile t+1 (K_{t+1}).  Scores of tile nkt are computed from a stale
+    // buffer and never used.  The probability registers swap roles every iteration
+    // (pA <-> pB), and so do the score registers.  With P = t mod NSTAGE a compile-time
+    // constant, the buffers an iteration reads are constants, which fold into the LDS reads'
+    // offset fields.  (The lambdas are always inlined: as calls, the register arrays they
+    // touch would go to scratch.)
+    auto body = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
+                    f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
         constexpr int P = decltype(phase)::value;
         constexpr unsigned k_next = ((P + 1) % C::NSTAGE) * C::TILE_BYTES;                // K_{t+1}
         constexpr unsigned v_prev = ((P + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES;    // V_{t-1}
-        load_k(t + C::NSTAGE);
-        load_v(t + C::NSTAGE - 2);
         if (t == 0) {
             stream<D, false, true, false>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
         } else {
@@ -636,35 +627,33 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             finish_softmax();
         }
         if (t + 1 < nkt) mask(s_next, next_valid());
-        __builtin_amdgcn_s_waitcnt(kWaitPrev);
+    };
+    // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
+    // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
+    // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
+    // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
+    // they wait for those loads, and the barrier publishes them.
+    static_assert(C::NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
+    auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
+        load_k(t + 3);
+        load_k(t + 4);
+        load_v(t + 1);
+        load_v(t + 2);
+        body(ph0, t, pA, pB, sB, sA);  // odd t: P_{t-1} in pA, S_t in sB
+        if (t + 1 < nkt) body(ph1, t + 1, pB, pA, sA, sB);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
     };
-    static_assert(C::NSTAGE == 4, "the unrolled loop below walks four phases");
     using Ph0 = std::integral_constant<int, 0>;
     using Ph1 = std::integral_constant<int, 1>;
     using Ph2 = std::integral_constant<int, 2>;
     using Ph3 = std::integral_constant<int, 3>;
-    iter(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
-    int t = 1;
-    // odd t: P.V with P_{t-1} = pA, softmax S_t (sB) -> pB, S_{t+1} -> sA; even t: the reverse
-    for (; t + 3 < nkt; t += 4) {
-        iter(Ph1{}, t, pA, pB, sB, sA);
-        iter(Ph2{}, t + 1, pB, pA, sA, sB);
-        iter(Ph3{}, t + 2, pA, pB, sB, sA);
-        iter(Ph0{}, t + 3, pB, pA, sA, sB);
-    }
-    // t = 1 mod 4 here: at most three more iterations, of phases 1, 2, 3
-    if (t < nkt) {
-        iter(Ph1{}, t, pA, pB, sB, sA);
-        ++t;
-    }
-    if (t < nkt) {
-        iter(Ph2{}, t, pB, pA, sA, sB);
-        ++t;
-    }
-    if (t < nkt) {
-        iter(Ph3{}, t, pA, pB, sB, sA);
-        ++t;
+    body(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
+    __syncthreads();                 // K_1's buffer is refilled by the first pair
+    // pairs (t, t+1) and (t+2, t+3); the last iterations may end a pair early
+    for (int t = 1; t < nkt; t += 4) {
+        pair(Ph1{}, Ph2{}, t);
+        if (t + 2 < nkt) pair(Ph3{}, Ph0{}, t + 2);
     }
     // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)
     if (nkt & 1)
