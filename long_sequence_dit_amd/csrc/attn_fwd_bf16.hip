@@ -143,7 +143,12 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// IEEE maximum (NaN-propagating): one v_maximum3_f32 per call, on raw MFMA results too.  (The
+// NaN-ignoring fmaxf needs its inputs quieted first, one more instruction per input that is not
+// already the result of a max.)  Row maxima of scores are the only use; a NaN score makes its
+// row NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 // bf16 pair {1, 1}
 __device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
@@ -310,20 +315,19 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
     } else if constexpr (POS == 2) {
         sm.mt[8] = max3(sel_f(s, 24), sel_f(s, 25), sel_f(s, 26));
         sm.mt[9] = max3(sel_f(s, 27), sel_f(s, 28), sel_f(s, 29));
-        // every raw score enters through a three-input max (a two-input max of raw MFMA
-        // results would first quiet each input, one more instruction apiece)
+        // every raw score enters through a three-input max: 32 scores in 16 v_maximum3
         sm.mt[10] = max3(sel_f(s, 30), sel_f(s, 31), sm.mt[0]);
         sm.mt[1] = max3(sm.mt[1], sm.mt[2], sm.mt[3]);
     } else if constexpr (POS == 3) {
         const float mx = max3(max3(sm.mt[1], sm.mt[4], sm.mt[5]), max3(sm.mt[6], sm.mt[7], sm.mt[8]),
-                              fmaxf(sm.mt[9], sm.mt[10]));
+                              vmax(sm.mt[9], sm.mt[10]));
         half_pair(mx, sm.m0, sm.m1);
     } else if constexpr (POS == 4) {
         // Lazy rescale: a row's reference max only moves when the row's max exceeds it by
         // more than kRescale (log2 units).  Weights are then at most 2^kRescale, harmless in
         // fp32 and bf16, and O and l stay consistent because both use the same reference.
         // Lanes l and l+32 hold the same row and take the same decision.
-        const float m_tile = __builtin_amdgcn_fmed3f(sm.m0, sm.m1, INFINITY) * w.c;  // max(m0, m1)
+        const float m_tile = vmax(sm.m0, sm.m1) * w.c;  // max(m0, m1)
         sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;

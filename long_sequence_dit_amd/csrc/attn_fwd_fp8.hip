@@ -92,7 +92,12 @@ __device__ __forceinline__ void half_pair(float x, float& a, float& b) {
     b = __uint_as_float(p[1]);
 }
 
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// IEEE maximum (NaN-propagating): one v_maximum3_f32 per call, on raw MFMA results too.  (The
+// NaN-ignoring fmaxf needs its inputs quieted first, one more instruction per input that is not
+// already the result of a max.)  Row maxima of scores are the only use; a NaN score makes its
+// row NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     bf16x2_t v;
@@ -242,12 +247,12 @@ __device__ __forceinline__ void softmax_slot(Wave& w, Soft& sm, const f32x16_t (
         sm.mt[1] = max3(sm.mt[1], sm.mt[2], sm.mt[3]);
     } else if constexpr (POS == 3) {
         const float mx = max3(max3(sm.mt[1], sm.mt[4], sm.mt[5]), max3(sm.mt[6], sm.mt[7], sm.mt[8]),
-                              fmaxf(sm.mt[9], sm.mt[10]));
+                              vmax(sm.mt[9], sm.mt[10]));
         float m0, m1;
         half_pair(mx, m0, m1);
         // lazy rescale: the reference moves only when the row max exceeds it by > kRescale,
         // so p <= 2^kRescale and 2^kPShift p fits E4M3; lanes l and l+32 agree
-        const float m_tile = __builtin_amdgcn_fmed3f(m0, m1, INFINITY) * w.c;
+        const float m_tile = vmax(m0, m1) * w.c;
         sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
