@@ -134,10 +134,14 @@ __device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int 
             : "memory");
 }
 
-// K tile rows (128 bytes) in LDS: 16-byte chunk c of row r sits at position c ^ (r & 7), so
-// the 8 lanes of one LDS cycle (8 consecutive rows, same chunk) hit 8 distinct bank groups.
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-// V^T tile rows (64 bytes, one per d): chunk c of row d at position c ^ ((d >> 2) & 3).
+// K tile rows (128 bytes, 8 chunks) in LDS: 16-byte chunk c of row r sits at position
+// c ^ k_swz(r).  An operand read has lanes on 32 consecutive rows at one logical chunk; with
+// c ^ (r & 7) alone, rows r and r + 8 land on the same banks (4 conflict cycles per read,
+// measured with SQ_LDS_BANK_CONFLICT); folding bits 3-4 of the row in separates them (0
+// measured).  Independent of row bit 5 (the key block), so key blocks stay 4 KiB apart.
+__device__ __forceinline__ int k_swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+// V^T tile rows (64 bytes, one per d): chunk c of row d at position c ^ ((d >> 2) & 3)
+// (0 conflict cycles measured).
 __device__ __forceinline__ int vt_swz(int d) { return (d >> 2) & 3; }
 
 // Key held at byte position (lane half h, byte b) of a P^T / V^T operand: byte b of a lane's
