@@ -150,8 +150,26 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 __device__ __forceinline__ float max3(float a, float b, float c) { return vmax(vmax(a, b), c); }
 
-// bf16 pair {1, 1}
-__device__ constexpr bf16x2_t kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+// Row sums on the matrix unit.  A lane's P^T fragment of one 16-key step (8 bf16: query
+// l % 32, keys of half l / 32) is also a valid B operand of v_mfma_f32_16x16x32_bf16, which
+// reads lane l as column l % 16 and k group l / 16: there the four lane groups hold queries
+// 0-15 and 16-31 of both key halves.  An A operand that is 1 where its k group's parity equals
+// bit 3 of its row sums, into rows 0-7 of column n, both key halves of query n, and into rows
+// 8-15 those of query n + 16.  The output puts rows 4 (l / 16) .. +3 of column l % 16 in lane
+// l, so lane l receives the row sum of query (l % 16) + 16 (l >= 32): its own query l % 32 for
+// lanes 0-15 and 48-63, the query of lane l - 16 (l + 16) for lanes 32-47 (16-31).  The sums are
+// those of the bf16 probabilities P.V uses, in fp32.
+__device__ __forceinline__ bf16x8_t rowsum_a_operand(int lane) {
+    const __bf16 v = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? (__bf16)1.0f : (__bf16)0.0f;
+    return bf16x8_t{v, v, v, v, v, v, v, v};
+}
+// The lane whose value belongs to the query lane l holds a row sum of (and the reverse).
+__device__ __forceinline__ int rowsum_partner(int lane) {
+    return lane < 16 || lane >= 48 ? lane : (lane < 32 ? lane + 16 : lane - 16);
+}
+__device__ __forceinline__ float from_lane(int src, float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(x)));
+}
 
 // Buffer resource of a K or V head: base, no stride, num_records bytes; reads past the
 // end return zeros.
@@ -237,7 +255,8 @@ struct Wave {
     f32x16_t acc[D / 32];  // O^T accumulators
     bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
     float m_run;           // reference max (scaled, log2 domain)
-    float l_run;           // this lane's share of the running row sum
+    f32x4_t lacc;          // row sums (every element; lanes 16-47 hold their partner's query)
+    bf16x8_t rs_a;         // A operand of the row-sum MFMA
     unsigned k_lane[D / 16];  // per-lane LDS read address of K operand kk in K buffer 0
     unsigned v_lane[D / 32];  // per-lane LDS read address of V^T operand dt in V buffer 0
     float c;               // scale * log2(e)
@@ -258,7 +277,7 @@ __host__ __device__ constexpr int last_a_slot() {
 struct Soft {
     float mt[11];           // partial maxima
     float m0, m1;           // row max of each half of the wave
-    float m_new, alpha, rs0, rs1;
+    float m_new, alpha;
     float x[16][2];         // stage A results (scaled, shifted scores)
     float e[16][2];         // stage B results (probabilities)
 };
@@ -293,10 +312,7 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
             pin(sm.e[J][0], sm.e[J][1]);
         } else if constexpr (POS == a + 2) {
             unsigned word = pack_bf16(sm.e[J][0], sm.e[J][1]);
-            float& rs = (J & 1) ? sm.rs1 : sm.rs0;
-            // the row sum adds the rounded probabilities that P.V uses: one dot2 per pair
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, word), kOnes, rs, false);
-            asm volatile("" : "+v"(word), "+v"(rs));
+            asm volatile("" : "+v"(word));
             p[J >> 2][J & 3] = word;
         }
         pair_stages<POS, LA, J + 1>(c, sm, s, p);
@@ -331,8 +347,6 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
         sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
-        sm.rs0 = 0.f;
-        sm.rs1 = 0.f;
     }
     pair_stages<POS, last_a_slot<D>()>(w.c, sm, s, p);
 }
@@ -385,6 +399,10 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned k
             w.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, op),
                                                                 __builtin_bit_cast(bf16x8_t, p_prev[ks]), w.acc[dt],
                                                                 0, 0, 0);
+            // the row sums of this 16-key step ride on the step's last P.V slot
+            if constexpr (dt == D / 32 - 1)
+                w.lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w.rs_a, __builtin_bit_cast(bf16x8_t, p_prev[ks]),
+                                                                 w.lacc, 0, 0, 0);
         } else {
             constexpr int sl = SLOT - C::N_PV, kk = sl >> 1, kb = sl & 1;
             if constexpr (kk == 0) {
@@ -471,7 +489,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     Wave<D> w;
     w.c = c;
     w.m_run = -INFINITY;
-    w.l_run = 0.f;
+    w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    w.rs_a = rowsum_a_operand(lane);
+    asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -595,14 +615,15 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     f32x16_t(&sB)[2] = kSpread ? sB_own : sA;
     u32x4_t pA[4], pB[4];
     Soft sm;
-    // after the softmax of a tile: running sum, and the rare rescale of the running output
+    // after the softmax of a tile: the rare rescale of the running output and row sums (the
+    // latter with the factor of the query whose sum the lane holds)
     auto finish_softmax = [&]() {
-        w.l_run = w.l_run * sm.alpha + (sm.rs0 + sm.rs1);
         if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
+            w.lacc *= from_lane(rowsum_partner(lane), sm.alpha);
         }
     };
     // tile 0: scores, then its softmax on its own
@@ -666,9 +687,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
 
     // ---- epilogue: normalise, LSE, store
-    float l0, l1;
-    half_pair(w.l_run, l0, l1);
-    const float l_tot = l0 + l1;
+    const float l_tot = from_lane(rowsum_partner(lane), w.lacc[0]);
     const float inv_l = 1.f / l_tot;
     const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
     if (qrow < a.Sq) {
