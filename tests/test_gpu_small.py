@@ -121,11 +121,12 @@ def test_max_chunks_random_lengths_and_order(dtype, mode):
     assert_parity(o, l, o_ref, l_ref, fp32=dtype == "fp32", what="64 chunks %s %s" % (dtype, mode))
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("Skv", [260, 512, 3000])
-def test_key_split_matches_unsplit(Skv):
+def test_key_split_matches_unsplit(Skv, D):
     """Few query tiles: the fused schedule splits the key tiles over several workgroups per
     query tile when given the workspace (and runs unsplit without it); both match the oracle."""
-    B, H, Sq, D = 1, 3, 200, 128
+    B, H, Sq = 1, 3, 200
     q, k, v = _inputs(B, H, Sq, Skv, D, seed=21)
     o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
@@ -136,6 +137,35 @@ def test_key_split_matches_unsplit(Skv):
         o, l = A().shard_fwd(qd, kd, vd, lens, (1, 0), mode="fused", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(o, l, o_ref, l_ref, what="Skv %d workspace %d" % (Skv, ws.numel()))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_rescale_on_every_tile(D):
+    """Key rows scaled up along the sequence, so that every 64-key tile's row max exceeds the
+    running reference by far more than the lazy-rescale threshold (2^8): the rescale of the
+    output and of the row sums runs on every tile, in every mode."""
+    B, H, Sq, Skv = 1, 2, 300, 900
+    q = synth.normal_rows(31, 0, B, H, Sq, D, kind=synth.KIND_F64)
+    k = synth.normal_rows(31, 1, B, H, Skv, D, kind=synth.KIND_F64)
+    v = synth.normal_rows(31, 2, B, H, Skv, D)
+    # every element of a query row has one sign and every key element is positive, growing along
+    # the keys: for the rows of positive sign the tile max grows by about 12 (log2 units) per
+    # tile, so those rows move their reference on 8 to 13 of the 13 tiles after the first (each
+    # wave rescales on every tile); rows of negative sign keep their first tile's max
+    q = synth.f32_to_bf16_bits((np.sign(q.sum(-1, keepdims=True)) * np.abs(q)).astype(np.float32))
+    k = synth.f32_to_bf16_bits((np.abs(k) * (0.05 + 11 * np.arange(Skv) / 64.0)[None, None, :, None] /
+                                math.sqrt(D)).astype(np.float32))
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle.attention(q, k, v, scale)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o, l = A().chunk_fwd(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    assert_parity(o, l, o_ref, l_ref, what="rescale every tile D=%d" % D)
+    for mode in ("fused", "nway", "online"):
+        ws = torch.empty(max(A().shard_workspace_size(B, H, Sq, D, 3, mode), 1), dtype=torch.uint8, device="cuda")
+        o, l = A().shard_fwd(qd, kd, vd, (300, 350, 250), (2, 0, 1), mode=mode, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(o, l, o_ref, l_ref, what="rescale every tile D=%d %s" % (D, mode))
 
 
 def test_bf16_chunk_partials_and_merge():
