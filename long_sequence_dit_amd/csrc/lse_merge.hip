@@ -12,7 +12,9 @@
 // loads), a row's D/4 lanes sit in one wave, and every part is read exactly
 // once.  Parts are taken in batches (2 to 16 parts, the smallest that covers
 // n, up to 16) with all of a batch's loads issued before any is used, so each
-// lane keeps a batch of loads in flight.
+// lane keeps a batch of loads in flight.  The parts are read, and the output written, once:
+// non-temporal accesses keep them from displacing other data in the caches (measured 5.4 ->
+// 5.8 TB/s for 8 parts of 44,160 x 16 rows).
 // Parts whose LSE is -inf carry no weight; if all are -inf the output is
 // O = 0, LSE = -inf.
 #include "kernels.h"
@@ -43,9 +45,9 @@ __device__ __forceinline__ void store4(void* o, Strides os, int o_bf16, int H, i
         u32x2_t w;
         w[0] = pack_bf16(x[0], x[1]);
         w[1] = pack_bf16(x[2], x[3]);
-        *(u32x2_t*)((unsigned short*)o + off) = w;
+        __builtin_nontemporal_store(w, (u32x2_t*)((unsigned short*)o + off));
     } else {
-        *(f32x4_t*)((float*)o + off) = x;
+        __builtin_nontemporal_store(x, (f32x4_t*)((float*)o + off));
     }
 }
 
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
                 const bool live = c0 + u < n;
-                x[u] = live ? *(const f32x4_t*)(a.o_parts[c0 + u] + row * a.D + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                x[u] = live ? __builtin_nontemporal_load((const f32x4_t*)(a.o_parts[c0 + u] + row * a.D + d))
+                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
                 w[u] = live ? a.lse_parts[c0 + u][row] : -INFINITY;
             }
 #pragma unroll
