@@ -21,9 +21,13 @@
 //    V^T must present the same keys in the same positions.  A pre-pass (fp8_pack_v) writes V
 //    as such V^T tiles (128 rows of d x 64 key bytes, already in the LDS layout), so every
 //    operand read is a plain 16-byte LDS read and every tile load is one contiguous 8 KiB.
-//  * The row sum is one more MFMA per tile: an all-ones A operand times P^T puts the sum of
-//    the E4M3 probabilities of each query row (the values P.V uses) in every accumulator
-//    element of that row's lanes.
+//  * The row sum is one more MFMA per tile, v_mfma_scale_f32_16x16x128_f8f6f4 (a quarter of
+//    the flops of the 32x32x64 form, half its cycles): a lane's P^T bytes are also a valid B
+//    operand there (column l % 16, k group l / 16: queries 0-15 and 16-31 of both key halves),
+//    and an A operand of E4M3 ones where the k group's parity equals bit 3 of the row sums both
+//    halves of query n into rows 0-7 of column n and those of query n + 16 into rows 8-15.  So
+//    the sum of the E4M3 probabilities (the values P.V uses) of query l % 32 lands in lane l
+//    for lanes 0-15 and 48-63, and in lane l + 16 (l - 16) for lanes 16-31 (32-47).
 //  * Probabilities are stored as E4M3(2^5 p): with the lazy rescale threshold 2^3, 2^5 p stays
 //    <= 256 (E4M3 tops out at 448), and probabilities down to 2^-11 of the reference are
 //    normal numbers; the 2^5 cancels in O = sum(P V) / sum(P) and is taken out of the LSE.
@@ -41,6 +45,7 @@ namespace lsdit {
 namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -75,6 +80,18 @@ constexpr int kPrefetch = 2;        // operands read this many slots ahead
 
 __device__ __forceinline__ f32x16_t mfma(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+// Row-sum MFMA (see the header): lane l's A bytes are ones where ((l >> 4) & 1) == bit 3 of l.
+__device__ __forceinline__ f32x4_t mfma_rowsum(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+// The lane whose row sum belongs to the query of lane l (and the reverse).
+__device__ __forceinline__ int rowsum_partner(int lane) {
+    return lane < 16 || lane >= 48 ? lane : (lane < 32 ? lane + 16 : lane - 16);
+}
+__device__ __forceinline__ float from_lane(int src, float x) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(x)));
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -190,9 +207,9 @@ __global__ __launch_bounds__(PACK_T) void fp8_pack_v_kernel(Fp8Args a, int n_kt)
 
 struct Wave {
     f32x16_t acc[D / 32];  // O^T accumulators
-    f32x16_t lacc;         // row sums (every element of a lane: its row's sum)
+    f32x4_t lacc;          // row sums (every element; lanes 16-47 hold their partner's query)
     i32x8_t qf[D / 64];    // Q bytes, B operands of the score MFMAs
-    i32x8_t ones;          // E4M3 ones, the A operand of the row-sum MFMA
+    i32x8_t rs_a;          // A operand of the row-sum MFMA
     float m_run;           // reference max (scaled, log2 domain)
     float c;               // scale * log2(e) * q_descale * k_descale
 };
@@ -311,7 +328,7 @@ __device__ __forceinline__ void stream_slots(Wave& w, const Addr& ad, unsigned v
         if constexpr (SLOT < 4) {
             w.acc[SLOT] = mfma(ring[read_idx(SLOT) % kPrefetch], p_prev, w.acc[SLOT]);
         } else if constexpr (SLOT == 4) {
-            w.lacc = mfma(w.ones, p_prev, w.lacc);
+            w.lacc = mfma_rowsum(w.rs_a, p_prev, w.lacc);
         } else {
             constexpr int sl = SLOT - N_PV, kk = sl >> 1, kb = sl & 1;
             if constexpr (kk == 0) {
@@ -378,11 +395,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
+    w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    {
+        const int ra = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? (int)kOnes : 0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) w.lacc[r] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) w.ones[r] = (int)kOnes;
-    asm volatile("" : "+v"(w.ones));  // kept in registers, not rebuilt before every use
+        for (int r = 0; r < 8; ++r) w.rs_a[r] = ra;
+    }
+    asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
 
     // Q bytes: lane (row, half h) holds d = 64 kk + 32 h .. +32 of its row
     const int qrow = qt * BQ + wave * 32 + (lane & 31);
@@ -468,8 +487,9 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
-            // only element 0 of the row sums is read; the others may drift
-            w.lacc[0] *= sm.alpha;
+            // only element 0 of the row sums is read; the others may drift.  The lane's row sum
+            // belongs to its partner's query, so it takes the partner's factor.
+            w.lacc[0] *= from_lane(rowsum_partner(lane), sm.alpha);
         }
     };
     stream<false, true, false>(w, ad, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
@@ -537,7 +557,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
 
     // epilogue: O = acc * v_descale / l, LSE = ln2 (m + log2 l - kPShift)
-    const float l_tot = w.lacc[0];
+    const float l_tot = from_lane(rowsum_partner(lane), w.lacc[0]);
     const float inv_l = a.v_descale / l_tot;
     const float lse2 = w.m_run + log2f(l_tot) - kPShift;
     if (qrow < a.Sq) {
