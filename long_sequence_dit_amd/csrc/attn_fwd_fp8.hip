@@ -225,10 +225,11 @@ __device__ __forceinline__ float sel_f(const f32x16_t (&s)[2], int f) { return s
 
 __device__ __forceinline__ void pin(float& a, float& b) { asm volatile("" : "+v"(a), "+v"(b)); }
 
-// Softmax schedule over the 9 slots of a stream: the max tree in slots 0-2, the reference
-// update in slot 3, then pair J of scores (2J, 2J+1) as a three-stage pipeline (FMA at a(J),
-// exp at a(J)+1, E4M3 pack at a(J)+2) with a(J) in 4..6.
-__host__ __device__ constexpr int pair_slot(int j) { return 4 + j / 6; }
+// Softmax schedule over the 9 slots of a stream: the max tree in slots 0-1 (the first key half,
+// whose last score MFMA ran a slot before the second half's, in slot 0), the reference update in
+// slot 2, then pair J of scores (2J, 2J+1) as a three-stage pipeline (FMA at a(J), exp at
+// a(J)+1, E4M3 pack at a(J)+2) with a(J) in 3..6: at most 8 exponentials per slot.
+__host__ __device__ constexpr int pair_slot(int j) { return 3 + j / 4; }
 
 template <int POS, int J = 0>
 __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&s)[2], i32x8_t& p) {
@@ -256,17 +257,15 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
 template <int POS>
 __device__ __forceinline__ void softmax_slot(Wave& w, Soft& sm, const f32x16_t (&s)[2], i32x8_t& p) {
     if constexpr (POS == 0) {
+        // scores 0-14 (the first key half, whose last MFMA ran a slot earlier than the second's)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
+        for (int i = 0; i < 5; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
     } else if constexpr (POS == 1) {
 #pragma unroll
-        for (int i = 4; i < 8; ++i) sm.mt[i] = max3(sel_f(s, 3 * i), sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2));
-    } else if constexpr (POS == 2) {
-        sm.mt[8] = max3(sel_f(s, 24), sel_f(s, 25), sel_f(s, 26));
-        sm.mt[9] = max3(sel_f(s, 27), sel_f(s, 28), sel_f(s, 29));
-        sm.mt[10] = max3(sel_f(s, 30), sel_f(s, 31), sm.mt[0]);
+        for (int i = 5; i < 10; ++i) sm.mt[i] = max3(sel_f(s, 3 * i + 1), sel_f(s, 3 * i + 2), sel_f(s, 3 * i + 3));
+        sm.mt[10] = max3(sel_f(s, 15), sel_f(s, 31), sm.mt[0]);
         sm.mt[1] = max3(sm.mt[1], sm.mt[2], sm.mt[3]);
-    } else if constexpr (POS == 3) {
+    } else if constexpr (POS == 2) {
         const float mx = max3(max3(sm.mt[1], sm.mt[4], sm.mt[5]), max3(sm.mt[6], sm.mt[7], sm.mt[8]),
                               vmax(sm.mt[9], sm.mt[10]));
         float m0, m1;
