@@ -127,9 +127,10 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
  * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd needs
  * for this shape, chunk count and merge mode: n fp32 partials (O and LSE) for
  * ATTN_MERGE_NWAY, two for ATTN_MERGE_ONLINE.  For ATTN_MERGE_FUSED (and any
- * mode when n_chunks == 1) no partials are needed; the size returned is the
- * room for splitting the key range of a shape with few query tiles on the
- * current device (0 when there is nothing to gain).
+ * mode when n_chunks == 1) no chunk partials are needed; the size returned is
+ * the room for the balanced tail (see attn_shard_fwd) of a shape whose query
+ * tiles of 256 rows leave the last round of the current device's CUs
+ * part-full: 2 * CUs * 256 * (D + 1) fp32 values (0 when they fill whole rounds).
  * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
  */
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
@@ -149,10 +150,13 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *   flags      one of ATTN_MERGE_NWAY, ATTN_MERGE_ONLINE, ATTN_MERGE_FUSED
  *              (ignored when n_chunks == 1).  FUSED is the ring's loop without
  *              partials: one kernel folds chunk after chunk into its running
- *              max, sum and output.  For shapes with few query tiles (bf16) it
- *              may also split the key tiles over several workgroups per query
- *              tile and merge their partials, as far as the workspace given
- *              allows (none given: no split).  ONLINE and NWAY run one kernel per chunk
+ *              max, sum and output.  When its query tiles (bf16, 256 rows)
+ *              leave the last round of CUs part-full and the keys are many,
+ *              that round's work is spread evenly instead: each CU takes an
+ *              equal run of (query tile, key tile) pairs, and a second kernel
+ *              merges the runs' fp32 partials by their LSE (the balanced tail;
+ *              only with the workspace: none given, whole tiles throughout).
+ *              ONLINE and NWAY run one kernel per chunk
  *              and merge the fp32 partials with attn_lse_merge's kernel, after
  *              every chunk (as a ring receiving one block per step does) or
  *              once at the end.

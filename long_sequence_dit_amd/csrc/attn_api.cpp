@@ -81,8 +81,6 @@ size_t slot_bytes(int32_t B, int32_t H, int32_t Sq, int32_t D) {
     return align_up(rows * D * 4) + align_up(rows * 4);
 }
 
-constexpr int kMaxSplit = 8;
-
 int device_cus() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -90,34 +88,34 @@ int device_cus() {
     return n;
 }
 
-// Workgroups per query tile for the bf16 kernel.  1 unless the B*H*ceil(Sq/256) query tiles
-// leave CUs idle in their last round; then the key tiles are split over k workgroups per
-// query tile (k <= kMaxSplit, >= 4 key tiles each), taking the k with the lowest estimated
-// time: the kernel at the CU occupancy k gives, plus (with_merge) writing and merging the k
-// fp32 partials.
-int choose_split(int64_t B, int64_t H, int64_t Sq, int64_t Skv, int D, int cus, bool with_merge) {
-    const int64_t n_q = B * H * ((Sq + 255) / 256);
-    const int64_t nkt = (Skv + 63) / 64;
-    if (n_q <= 0 || n_q >= 4 * (int64_t)cus) return 1;
-    auto occupancy = [&](int64_t k) {
-        const int64_t wgs = n_q * k, rounds = (wgs + cus - 1) / cus;
-        return (double)wgs / (double)(rounds * cus);
-    };
-    const double flops = 4.0 * (double)B * H * Sq * (double)Skv * D;
-    const double rate = 1.0e15, bw = 5.0e12;  // kernel FLOP/s at full occupancy; merge bytes/s
-    const double rows = (double)B * H * Sq;
-    double best_t = flops / (rate * occupancy(1));
-    int best = 1;
-    for (int k = 2; k <= kMaxSplit && 4 * k <= nkt; ++k) {
-        double t = flops / (rate * occupancy(k));
-        if (with_merge) t += rows * (2.0 * k * (D + 1) * 4 + D * 2 + 4) / bw;
-        if (t < 0.98 * best_t) {
-            best_t = t;
-            best = k;
-        }
-    }
-    return best;
+// The balanced tail of the bf16 kernel (FwdArgs): when its n_q query tiles leave CUs idle in
+// the last round, the full rounds run whole query tiles and the last round's work is spread
+// evenly over the CUs as runs of (query tile, key tile) units, whose partials the fix-up kernel
+// merges.  Worth it when the idle part of the last round is at least kSkMinSaving key tiles
+// per CU: the runs' pipeline fill and drain, their partials and the fix-up launch cost about
+// as much as 20-30 key tiles (at 22 tiles, the 4,608-token image shape ran 4.5% slower with the
+// tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).
+struct SkPlan {
+    int n_dp = 0;    // query tiles run whole
+    int sk_wgs = 0;  // workgroups of the tail (0 = no tail)
+};
+constexpr int64_t kSkMinSaving = 64;
+
+SkPlan sk_plan(int64_t n_q, int64_t T, int cus) {
+    SkPlan p;
+    if (n_q <= 0 || T <= 0 || cus <= 0 || n_q > 0x7FFFFFFF) return p;
+    const int64_t rem = n_q % cus;
+    if (rem == 0 || T * (cus - rem) / cus < kSkMinSaving) return p;
+    const int64_t U = rem * T;  // > rem, since T >= kSkMinSaving: every run is at most T long
+    p.n_dp = (int)(n_q - rem);
+    p.sk_wgs = (int)(U < cus ? U : cus);
+    return p;
 }
+
+// Query tiles of the bf16 kernel, and the workspace of its tail: 2 slots per workgroup.
+int64_t n_qtiles(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows); }
+size_t sk_o_bytes(int sk_wgs, int D) { return align_up((size_t)2 * sk_wgs * lsdit::kSkRows * D * 4); }
+size_t sk_bytes(int sk_wgs, int D) { return sk_o_bytes(sk_wgs, D) + align_up((size_t)2 * sk_wgs * lsdit::kSkRows * 4); }
 
 int slots_for(uint32_t flags, int32_t n) {
     if (n <= 1) return 0;
@@ -154,7 +152,6 @@ attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, at
     a.n_chunks = 1;
     a.chunk_row[0] = 0;
     a.chunk_len[0] = Skv;
-    a.n_split = 1;
     return run_fwd(a, in_dt, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
@@ -184,9 +181,11 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags) {
     if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
     if (flags == ATTN_MERGE_FUSED || n_chunks == 1) {
-        // room for the key split of few-query-tile shapes (largest split over any key count)
-        const int k = choose_split(B, H, Sq, (int64_t)1 << 40, D, device_cus(), false);
-        return k > 1 ? (size_t)k * slot_bytes(B, H, Sq, D) : 0;
+        // room for the balanced tail of shapes whose query tiles leave the last round part-full
+        // (whether it runs also depends on the key count)
+        const int cus = device_cus();
+        const int64_t n_q = n_qtiles(B, H, Sq);
+        return n_q % cus != 0 ? sk_bytes(cus, D) : 0;
     }
     const int slots = slots_for(flags, n_chunks);
     if (slots <= 0) return 0;
@@ -243,7 +242,6 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     base.q = q; base.k = k; base.v = v;
     base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
     base.B = B; base.H = H; base.Sq = Sq; base.Skv = (int32_t)total; base.D = D; base.scale = scale;
-    base.n_split = 1;
     auto chunk_args = [&](int c) {  // one chunk, by its rows in the k and v tensors
         FwdArgs a = base;
         a.n_chunks = 1;
@@ -272,29 +270,29 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
             a.chunk_row[t] = (int32_t)off[live[t]];
             a.chunk_len[t] = chunk_len[live[t]];
         }
-        // few query tiles: split the key tiles over k workgroups per query tile, as far as
-        // the workspace allows, and merge the k partials
-        int k = in_dt == ATTN_BF16 ? choose_split(B, H, Sq, total, D, device_cus(), true) : 1;
-        const size_t sb = slot_bytes(B, H, Sq, D);
+        to_final(a);
+        // query tiles that leave the last round part-full: spread that round's work evenly
+        // (the balanced tail), as far as the workspace allows
         const bool ws_ok = workspace && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0;
-        while (k > 1 && (!ws_ok || ws_bytes < (size_t)k * sb)) --k;
-        if (k == 1) {
-            to_final(a);
+        int64_t T = 0;  // key tiles of the chunk list, as the kernel counts them
+        for (int t = 0; t < n_live; ++t) T += (chunk_len[live[t]] + 63) / 64;
+        const int64_t n_q = n_qtiles(B, H, Sq);
+        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, device_cus()) : SkPlan{};
+        if (p.sk_wgs == 0 || !ws_ok || ws_bytes < sk_bytes(p.sk_wgs, D))
             return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
-        }
-        a.n_split = k;
-        a.o = slot_o(0); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(0);
-        a.split_o_stride = a.split_lse_stride = (int64_t)(sb / 4);
+        a.n_dp = p.n_dp;
+        a.sk_wgs = p.sk_wgs;
+        a.sk_o = (float*)workspace;
+        a.sk_lse = (float*)((char*)workspace + sk_o_bytes(p.sk_wgs, D));
         if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
-        MergeArgs m{};
-        m.B = B; m.H = H; m.Sq = Sq; m.D = D;
-        m.n = k;
-        for (int i = 0; i < k; ++i) {
-            m.o_parts[i] = slot_o(i);
-            m.lse_parts[i] = slot_lse(i);
-        }
-        m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
-        return ok(lsdit::launch_lse_merge(m, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        lsdit::SkFixupArgs f{};
+        f.B = B; f.H = H; f.Sq = Sq; f.D = D;
+        f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
+        f.T = (int)T;
+        f.n_dp = p.n_dp; f.n_q = (int)n_q; f.sk_wgs = p.sk_wgs;
+        f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
+        f.o = o; f.os = S(os); f.o_bf16 = o_dt == ATTN_BF16; f.lse = lse;
+        return ok(lsdit::launch_sk_fixup(f, s)) ? ATTN_OK : ATTN_ERR_HIP;
     }
 
     MergeArgs m{};

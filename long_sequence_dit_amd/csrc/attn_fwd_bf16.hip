@@ -69,6 +69,9 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+// Kernel arguments seen through the constant address space (scalar loads).
+template <class T>
+using kernarg_t = __attribute__((address_space(4))) const T;
 
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
@@ -291,6 +294,17 @@ struct Soft {
 // the next tile overwrite them.
 __host__ __device__ constexpr int pair_slot(int j, int la) { return 5 + j * (la - 4) / 16; }
 
+// One probability buffer serves both the P.V of tile t-1 (reading it) and the softmax of tile t
+// (writing it): P.V reads word group ks of P^T in slots ks*(D/32) .. ks*(D/32) + D/32 - 1, and
+// the first pack into group ks (pair 4ks's stage C) comes in a later slot.
+template <int D>
+__host__ __device__ constexpr bool one_p_buffer_suffices() {
+    for (int ks = 0; ks < 4; ++ks)
+        if (pair_slot(4 * ks, last_a_slot<D>()) + 2 <= ks * (D / 32) + D / 32 - 1) return false;
+    return true;
+}
+static_assert(one_p_buffer_suffices<128>() && one_p_buffer_suffices<64>(), "probability buffer reused too early");
+
 // Empty asm statements (register operands only) pin a stage's results to its slot: the
 // scheduling barriers order instructions, but pure arithmetic could still be sunk towards
 // its use.  Only results are pinned: pinning an input read out of a live score vector would
@@ -457,19 +471,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hi = lane >> 5;  // which half of the wave (MFMA k-half)
-    // grid = n_split groups of B*H*n_qt query tiles; the split index varies slowest, so each
-    // XCD's contiguous share of the remapped grid reads one key range of few heads
-    const int gidx = xcd_remap(blockIdx.x, gridDim.x);
     const int n_qtiles = a.B * a.H * n_qt;
-    const int split = gidx / n_qtiles, tile = gidx % n_qtiles;
-    const int bh = tile / n_qt, qt = tile % n_qt;
-    const int b = bh / a.H, h = bh % a.H;
-
-    const unsigned short* qp = (const unsigned short*)a.q + b * a.qs.b + h * a.qs.h;
-    const unsigned short* kp = (const unsigned short*)a.k + b * a.ks.b + h * a.ks.h;
-    const unsigned short* vp = (const unsigned short*)a.v + b * a.vs.b + h * a.vs.h;
     const int Skv = a.Skv;  // key rows of the k and v tensors
+    static_assert(C::BQ == kSkRows, "stream-K slots hold one query tile");
 
     // ---- the chunk list: lane c holds chunk c's first row and length (read through the
     // kernel-argument pointer, so the argument array is not copied to registers first)
@@ -482,241 +486,301 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     const int v_len = lane < n_chunks ? arg_lens[lane] : 0;
     int nkt_all = 0;  // tiles over all chunks
     for (int ci = 0; ci < n_chunks; ++ci) nkt_all += (__builtin_amdgcn_readlane(v_len, ci) + C::BK - 1) / C::BK;
-    // this workgroup's share of the tile sequence
-    const int g_first = (int)((int64_t)split * nkt_all / a.n_split);
-    const int nkt = (int)((int64_t)(split + 1) * nkt_all / a.n_split) - g_first;
 
-    Wave<D> w;
-    w.c = c;
-    w.m_run = -INFINITY;
-    w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    w.rs_a = rowsum_a_operand(lane);
-    asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
-
-    // ---- Q fragments: B operand, lane holds Q[row][16kk + 8hi .. +8]
-    const int qrow = qt * C::BQ + wave * 32 + (lane & 31);
-    const int qrow_c = qrow < a.Sq ? qrow : a.Sq - 1;
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
-        w.qf[kk] = *(const bf16x8_t*)(qp + (int64_t)qrow_c * a.qs.s + 16 * kk + 8 * hi);
-
-    // ---- K/V loads straight into LDS.  One wave-wide instruction fills a contiguous
-    // 1 KiB block (lane L -> bytes 16L..16L+15); lane L fetches the global chunk that the
-    // swizzle maps to its slot.  Offsets are per lane and fixed; tiles advance by a scalar.
-    // Loads of tiles past the chunk fall outside the buffer and read zeros.
-    const int k_rs = (int)(a.ks.s * 2), v_rs = (int)(a.vs.s * 2);  // row pitch in bytes
-    const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D * 2);
-    const Rsrc vrs = make_rsrc(vp, (Skv - 1) * v_rs + D * 2);
-    int k_goff[C::BLKS_PER_WAVE], v_goff[C::BLKS_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < C::BLKS_PER_WAVE; ++i) {
-        const int blk = wave * C::BLKS_PER_WAVE + i;
-        const int row = blk * C::ROWS_PER_BLK + lane / C::CH, slot = lane % C::CH;
-        k_goff[i] = row * k_rs + (slot ^ k_swz<D>(row)) * 16;
-        v_goff[i] = row * v_rs + (slot ^ v_swz<D>(row)) * 16;
-    }
-    // The kernel declares no static LDS, so its dynamic block (smem) starts at LDS address 0
-    // and every LDS access below is a plain byte address; a CPU test checks that the built
-    // kernel has no static LDS.  (Pointer arithmetic on smem instead costs one add per
-    // address: the block's address is a link-time constant the compiler cannot fold.)
-    (void)smem;
-    constexpr unsigned lds_base = 0;
-    // Offsets of tile t's buffers within the K region (LDS address 0) and the V region (LDS
-    // address V_REGION)
-    auto kbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
-    auto vbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
-    // Three walks over the tile sequence: the next K tile to load (tile t + NSTAGE during
-    // iteration t), the next V tile to load (tile t + NSTAGE - 2) and the next tile to mask
-    // (tile t + 1).  Tile g of the sequence goes into buffer g mod NSTAGE.
-    TileWalk<C::BK> wk, wv, wm;
-    wk.seek(g_first, n_chunks, v_row, v_len, Skv);
-    wv = wk;
-    wm = wk;
-    auto load_k = [&](int g) {
-        if (wave < C::LOADERS)
-            lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
-        wk.next(n_chunks, v_row, v_len, Skv);
-    };
-    auto load_v = [&](int g) {
-        if (wave < C::LOADERS)
-            lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + C::V_REGION + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff,
-                                      wv.row * v_rs);
-        wv.next(n_chunks, v_row, v_len, Skv);
-    };
-    auto next_valid = [&]() {  // valid keys of the next tile to mask
-        const int valid = wm.valid();
-        wm.next(n_chunks, v_row, v_len, Skv);
-        return valid;
-    };
-
-    // ---- per-lane LDS read addresses in buffer 0 of each region.  Each swizzle XOR only
-    // touches chunk-index bits that the operand index sets independently, so the operand
-    // index enters as an XOR with a constant (taken once here, one register per operand
-    // column) and row steps, key blocks and buffers as additions (folded into the reads'
-    // offset fields).
-    // K operand (kb, kk): row kb*32 + (lane&31), chunk 2kk + hi  ->  k_base ^ (kk << 5)
-    // (k_swz(row + 32) == k_swz(row)).
-    {
-        const unsigned k_base = (lane & 31) * C::ROW_BYTES + ((hi ^ k_swz<D>(lane & 31)) * 16);
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) w.k_lane[kk] = k_base ^ (kk << 5);
-    }
-    // V^T operand (dt, ks, lo/hi): rows 16ks + 4(g>>1) + (j>>2) (+8), element columns
-    // 32dt + 16(g&1) + 4(j&3)  ->  v_base ^ (dt << 6); v_swz depends on row & 3 only.
-    {
-        const int g = lane >> 4, j = lane & 15;
-        const int v_row0 = 4 * (g >> 1) + (j >> 2);
-        const int v_col0 = 16 * (g & 1) + 4 * (j & 3);
-        const unsigned v_base = v_row0 * C::ROW_BYTES + (((v_col0 >> 3) ^ v_swz<D>(v_row0)) * 16) + (v_col0 & 7) * 2;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) w.v_lane[dt] = C::V_REGION + (v_base ^ (dt << 6));
-    }
-    // opaque to the compiler, so the offsets stay additions folded into the reads' offset
-    // fields (with their bits known disjoint it may turn them into ORs computed per read)
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(w.k_lane[kk]));
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(w.v_lane[dt]));
-
-    // Key of accumulator element (kb, r) is kb*32 + 8(r>>2) + 4hi + (r&3); compare its
-    // compile-time part against valid - 4hi, so no table of per-lane key indices is kept live.
-    // Rows of a tile past its chunk's end (another chunk's keys, or zeros past the tensor)
-    // get P = 0.
-    auto mask = [&](f32x16_t(&s)[2], int valid) {
-        if (valid < C::BK) {
-            const int lim = valid - 4 * hi;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
-        }
-    };
-
-    // ---- prologue.  Zero the tiles first: key rows past the end of a chunk are masked
-    // (P = 0), and zeros there keep 0 * V finite whatever the loads leave in those rows.
-    for (int i = tid; i < C::LDS_BYTES / 16; i += C::NT)
-        *(lds_u32x4_t*)(size_t)(lds_base + 16u * i) = u32x4_t{0u, 0u, 0u, 0u};
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < C::NSTAGE; ++g) load_k(g);
-#pragma unroll
-    for (int g = 0; g < C::NSTAGE / 2; ++g) load_v(g);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
-    __syncthreads();
-
-    // Scores of alternate tiles (one buffer without kSpread: the softmax of tile t then reads
-    // it before the score MFMAs of tile t+1 overwrite it) and probabilities of alternate tiles.
-    f32x16_t sA[2], sB_own[2];
-    f32x16_t(&sB)[2] = kSpread ? sB_own : sA;
-    u32x4_t pA[4], pB[4];
-    Soft sm;
-    // after the softmax of a tile: the rare rescale of the running output and row sums (the
-    // latter with the factor of the query whose sum the lane holds)
-    auto finish_softmax = [&]() {
-        if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
-            w.lacc *= from_lane(rowsum_partner(lane), sm.alpha);
-        }
-    };
-    // tile 0: scores, then its softmax on its own
-    stream<D, false, true, false>(w, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
-    mask(sA, next_valid());
-    softmax_all<D>(w, sm, sA, pA);  // P_0 -> pA
-    finish_softmax();
-    __syncthreads();  // every wave is done with K buffer 0 before tile NSTAGE overwrites it
-
-    // ---- key loop.  Iteration t streams P.V of tile t-1 (V_{t-1}) with the softmax of tile t,
-    // then the scores of tile t+1 (K_{t+1}).  Scores of tile nkt are computed from a stale
-    // buffer and never used.  The probability registers swap roles every iteration
-    // (pA <-> pB), and so do the score registers.  With P = t mod NSTAGE a compile-time
-    // constant, the buffers an iteration reads are constants, which fold into the LDS reads'
-    // offset fields.  (The lambdas are always inlined: as calls, the register arrays they
-    // touch would go to scratch.)
-    auto body = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
-                    f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
-        constexpr int P = decltype(phase)::value;
-        constexpr unsigned k_next = ((P + 1) % C::NSTAGE) * C::TILE_BYTES;                // K_{t+1}
-        constexpr unsigned v_prev = ((P + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES;    // V_{t-1}
-        if (t == 0) {
-            stream<D, false, true, false>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+    // ---- this workgroup's work: segments (query tile, run of the key-tile sequence).
+    // Without a stream-K tail the grid is the B*H*n_qt query tiles, one whole tile each.  With
+    // one, workgroups below n_dp take whole query tiles (remapped over that part alone: the
+    // tail's workgroups follow in dispatch order) and the others an equal run of the tail's
+    // units, which spans at most two query tiles.
+    // Only seg is carried from one segment to the next: each iteration derives its segment from
+    // the workgroup index again (state kept live across the key loop would cost registers).
+    for (int seg = 0;; ++seg) {
+        // the arguments, read through a pointer the compiler cannot follow: so their loads stay
+        // in the iteration rather than being hoisted in front of the loop and held in registers
+        // across it
+        const kernarg_t<FwdArgs>* ap = (const kernarg_t<FwdArgs>*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        const kernarg_t<FwdArgs>& ar = *ap;
+        // likewise the lane index: values derived from it are computed in the iteration
+        int lane_it = lane;
+        asm volatile("" : "+v"(lane_it));
+        const int hi_it = lane_it >> 5;
+        int sk_w = -1, tile, g_first, nkt;
+        if (ar.sk_wgs == 0 || (int)blockIdx.x < ar.n_dp) {
+            if (seg > 0) break;
+            tile = xcd_remap(blockIdx.x, ar.sk_wgs == 0 ? n_qtiles : ar.n_dp);
+            g_first = 0;
+            nkt = nkt_all;
         } else {
-            stream<D, true, true, true>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
-            finish_softmax();
+            sk_w = xcd_remap(blockIdx.x - ar.n_dp, ar.sk_wgs);
+            const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
+            const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
+            // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1
+            const int64_t cut = (u0 / nkt_all + 1) * nkt_all;
+            const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
+            if (seg > 1 || s0 >= s1) break;
+            tile = ar.n_dp + (int)(s0 / nkt_all);
+            g_first = (int)(s0 % nkt_all);
+            nkt = (int)(s1 - s0);
         }
-        if (t + 1 < nkt) mask(s_next, next_valid());
-    };
-    // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
-    // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
-    // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
-    // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
-    // they wait for those loads, and the barrier publishes them.
-    static_assert(C::NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
-    auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
-        load_k(t + 3);
-        load_k(t + 4);
-        load_v(t + 1);
-        load_v(t + 2);
-        body(ph0, t, pA, pB, sB, sA);  // odd t: P_{t-1} in pA, S_t in sB
-        if (t + 1 < nkt) body(ph1, t + 1, pB, pA, sA, sB);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // wave-uniform: the 64-bit divisions above run on the vector unit, and left there the
+        // key loop's control flow derived from these would become per-lane
+        tile = __builtin_amdgcn_readfirstlane(tile);
+        g_first = __builtin_amdgcn_readfirstlane(g_first);
+        nkt = __builtin_amdgcn_readfirstlane(nkt);
+        sk_w = __builtin_amdgcn_readfirstlane(sk_w);
+        if (seg > 0) {
+            // every wave is done with the previous segment's tiles (and no load is in flight)
+            // before this segment's prologue rewrites LDS
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+        }
+        const int bh = tile / n_qt, qt = tile % n_qt;
+        const int b = bh / ar.H, h = bh % ar.H;
+        const unsigned short* qp = (const unsigned short*)ar.q + b * ar.qs.b + h * ar.qs.h;
+        const unsigned short* kp = (const unsigned short*)ar.k + b * ar.ks.b + h * ar.ks.h;
+        const unsigned short* vp = (const unsigned short*)ar.v + b * ar.vs.b + h * ar.vs.h;
+
+        Wave<D> w;
+        w.c = c;
+        w.m_run = -INFINITY;
+        w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        w.rs_a = rowsum_a_operand(lane_it);
+        asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
+
+        // ---- Q fragments: B operand, lane_it holds Q[row][16kk + 8hi .. +8]
+        const int qrow = qt * C::BQ + wave * 32 + (lane_it & 31);
+        const int qrow_c = qrow < ar.Sq ? qrow : ar.Sq - 1;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            w.qf[kk] = *(const bf16x8_t*)(qp + (int64_t)qrow_c * ar.qs.s + 16 * kk + 8 * hi_it);
+
+        // ---- K/V loads straight into LDS.  One wave-wide instruction fills a contiguous
+        // 1 KiB block (lane_it L -> bytes 16L..16L+15); lane_it L fetches the global chunk that the
+        // swizzle maps to its slot.  Offsets are per lane_it and fixed; tiles advance by a scalar.
+        // Loads of tiles past the chunk fall outside the buffer and read zeros.
+        const int k_rs = (int)(ar.ks.s * 2), v_rs = (int)(ar.vs.s * 2);  // row pitch in bytes
+        const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D * 2);
+        const Rsrc vrs = make_rsrc(vp, (Skv - 1) * v_rs + D * 2);
+        int k_goff[C::BLKS_PER_WAVE], v_goff[C::BLKS_PER_WAVE];
+#pragma unroll
+        for (int i = 0; i < C::BLKS_PER_WAVE; ++i) {
+            const int blk = wave * C::BLKS_PER_WAVE + i;
+            const int row = blk * C::ROWS_PER_BLK + lane_it / C::CH, slot = lane_it % C::CH;
+            k_goff[i] = row * k_rs + (slot ^ k_swz<D>(row)) * 16;
+            v_goff[i] = row * v_rs + (slot ^ v_swz<D>(row)) * 16;
+        }
+        // The kernel declares no static LDS, so its dynamic block (smem) starts at LDS address 0
+        // and every LDS access below is a plain byte address; a CPU test checks that the built
+        // kernel has no static LDS.  (Pointer arithmetic on smem instead costs one add per
+        // address: the block's address is a link-time constant the compiler cannot fold.)
+        (void)smem;
+        constexpr unsigned lds_base = 0;
+        // Offsets of tile t's buffers within the K region (LDS address 0) and the V region (LDS
+        // address V_REGION)
+        auto kbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
+        auto vbuf = [&](int t) { return (unsigned)((t % C::NSTAGE) * C::TILE_BYTES); };
+        // Three walks over the tile sequence: the next K tile to load (tile t + NSTAGE during
+        // iteration t), the next V tile to load (tile t + NSTAGE - 2) and the next tile to mask
+        // (tile t + 1).  Tile g of the sequence goes into buffer g mod NSTAGE.
+        TileWalk<C::BK> wk, wv, wm;
+        wk.seek(g_first, n_chunks, v_row, v_len, Skv);
+        wv = wk;
+        wm = wk;
+        auto load_k = [&](int g) {
+            if (wave < C::LOADERS)
+                lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
+            wk.next(n_chunks, v_row, v_len, Skv);
+        };
+        auto load_v = [&](int g) {
+            if (wave < C::LOADERS)
+                lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + C::V_REGION + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff,
+                                          wv.row * v_rs);
+            wv.next(n_chunks, v_row, v_len, Skv);
+        };
+        auto next_valid = [&]() {  // valid keys of the next tile to mask
+            const int valid = wm.valid();
+            wm.next(n_chunks, v_row, v_len, Skv);
+            return valid;
+        };
+
+        // ---- per-lane_it LDS read addresses in buffer 0 of each region.  Each swizzle XOR only
+        // touches chunk-index bits that the operand index sets independently, so the operand
+        // index enters as an XOR with a constant (taken once here, one register per operand
+        // column) and row steps, key blocks and buffers as additions (folded into the reads'
+        // offset fields).
+        // K operand (kb, kk): row kb*32 + (lane_it&31), chunk 2kk + hi_it  ->  k_base ^ (kk << 5)
+        // (k_swz(row + 32) == k_swz(row)).
+        {
+            const unsigned k_base = (lane_it & 31) * C::ROW_BYTES + ((hi_it ^ k_swz<D>(lane_it & 31)) * 16);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk) w.k_lane[kk] = k_base ^ (kk << 5);
+        }
+        // V^T operand (dt, ks, lo/hi_it): rows 16ks + 4(g>>1) + (j>>2) (+8), element columns
+        // 32dt + 16(g&1) + 4(j&3)  ->  v_base ^ (dt << 6); v_swz depends on row & 3 only.
+        {
+            const int g = lane_it >> 4, j = lane_it & 15;
+            const int v_row0 = 4 * (g >> 1) + (j >> 2);
+            const int v_col0 = 16 * (g & 1) + 4 * (j & 3);
+            const unsigned v_base = v_row0 * C::ROW_BYTES + (((v_col0 >> 3) ^ v_swz<D>(v_row0)) * 16) + (v_col0 & 7) * 2;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) w.v_lane[dt] = C::V_REGION + (v_base ^ (dt << 6));
+        }
+        // opaque to the compiler, so the offsets stay additions folded into the reads' offset
+        // fields (with their bits known disjoint it may turn them into ORs computed per read)
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(w.k_lane[kk]));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) asm volatile("" : "+v"(w.v_lane[dt]));
+
+        // Key of accumulator element (kb, r) is kb*32 + 8(r>>2) + 4hi + (r&3); compare its
+        // compile-time part against valid - 4hi, so no table of per-lane_it key indices is kept live.
+        // Rows of a tile past its chunk's end (another chunk's keys, or zeros past the tensor)
+        // get P = 0.
+        auto mask = [&](f32x16_t(&s)[2], int valid) {
+            if (valid < C::BK) {
+                const int lim = valid - 4 * hi_it;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+            }
+        };
+
+        // ---- prologue.  Zero the tiles first: key rows past the end of a chunk are masked
+        // (P = 0), and zeros there keep 0 * V finite whatever the loads leave in those rows.
+        for (int i = (wave * 64 + lane_it); i < C::LDS_BYTES / 16; i += C::NT)
+            *(lds_u32x4_t*)(size_t)(lds_base + 16u * i) = u32x4_t{0u, 0u, 0u, 0u};
         __syncthreads();
-    };
-    using Ph0 = std::integral_constant<int, 0>;
-    using Ph1 = std::integral_constant<int, 1>;
-    using Ph2 = std::integral_constant<int, 2>;
-    using Ph3 = std::integral_constant<int, 3>;
-    body(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
-    __syncthreads();                 // K_1's buffer is refilled by the first pair
-    // pairs (t, t+1) and (t+2, t+3); the last iterations may end a pair early
-    for (int t = 1; t < nkt; t += 4) {
-        pair(Ph1{}, Ph2{}, t);
-        if (t + 2 < nkt) pair(Ph3{}, Ph0{}, t + 2);
-    }
-    // P.V of the last tile, whose probabilities sit in pA (nkt odd) or pB (nkt even)
-    if (nkt & 1)
-        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
-    else
-        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
+#pragma unroll
+        for (int g = 0; g < C::NSTAGE; ++g) load_k(g);
+#pragma unroll
+        for (int g = 0; g < C::NSTAGE / 2; ++g) load_v(g);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, the chunk table and the first tiles are in
+        __syncthreads();
 
-    // ---- epilogue: normalise, LSE, store
-    const float l_tot = from_lane(rowsum_partner(lane), w.lacc[0]);
-    const float inv_l = 1.f / l_tot;
-    const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
-    if (qrow < a.Sq) {
-        if (a.o_bf16) {
-            unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;  // no split
+        // Scores of alternate tiles (one buffer without kSpread: the softmax of tile t then reads
+        // it before the score MFMAs of tile t+1 overwrite it) and probabilities of alternate tiles.
+        f32x16_t sA[2], sB_own[2];
+        f32x16_t(&sB)[2] = kSpread ? sB_own : sA;
+        u32x4_t pp[4];  // probabilities (one buffer suffices: see one_p_buffer_suffices)
+        Soft sm;
+        // after the softmax of a tile: the rare rescale of the running output and row sums (the
+        // latter with the factor of the query whose sum the lane_it holds)
+        auto finish_softmax = [&]() {
+            if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * dt + 8 * r4 + 4 * hi;
-                    u32x2_t wd;
-                    wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
-                    wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
-                    *(u32x2_t*)(op + d) = wd;
-                }
-        } else {
-            float* op = (float*)a.o + split * a.split_o_stride + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * dt + 8 * r4 + 4 * hi;
-                    f32x4_t x;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * inv_l;
-                    *(f32x4_t*)(op + d) = x;
-                }
+                    for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
+                w.lacc *= from_lane(rowsum_partner(lane_it), sm.alpha);
+            }
+        };
+        // tile 0: scores, then its softmax on its own
+        stream<D, false, true, false>(w, vbuf(0), kbuf(0), pp, sA, sA, pp, sm);  // S_0 -> sA
+        mask(sA, next_valid());
+        softmax_all<D>(w, sm, sA, pp);  // P_0
+        finish_softmax();
+        __syncthreads();  // every wave is done with K buffer 0 before tile NSTAGE overwrites it
+
+        // ---- key loop.  Iteration t streams P.V of tile t-1 (V_{t-1}) with the softmax of tile t,
+        // then the scores of tile t+1 (K_{t+1}).  Scores of tile nkt are computed from a stale
+        // buffer and never used.  The score registers swap roles every iteration (sA <->
+        // sB); the probability registers are one buffer.  With P = t mod NSTAGE a compile-time
+        // constant, the buffers an iteration reads are constants, which fold into the LDS reads'
+        // offset fields.  (The lambdas are always inlined: as calls, the register arrays they
+        // touch would go to scratch.)
+        auto body = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
+                        f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
+            constexpr int P = decltype(phase)::value;
+            constexpr unsigned k_next = ((P + 1) % C::NSTAGE) * C::TILE_BYTES;                // K_{t+1}
+            constexpr unsigned v_prev = ((P + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES;    // V_{t-1}
+            if (t == 0) {
+                stream<D, false, true, false>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+            } else {
+                stream<D, true, true, true>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+                finish_softmax();
+            }
+            if (t + 1 < nkt) mask(s_next, next_valid());
+        };
+        // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
+        // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
+        // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
+        // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
+        // they wait for those loads, and the barrier publishes them.
+        static_assert(C::NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
+        auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
+            load_k(t + 3);
+            load_k(t + 4);
+            load_v(t + 1);
+            load_v(t + 2);
+            body(ph0, t, pp, pp, sB, sA);  // odd t: S_t in sB
+            if (t + 1 < nkt) body(ph1, t + 1, pp, pp, sA, sB);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+        };
+        using Ph0 = std::integral_constant<int, 0>;
+        using Ph1 = std::integral_constant<int, 1>;
+        using Ph2 = std::integral_constant<int, 2>;
+        using Ph3 = std::integral_constant<int, 3>;
+        body(Ph0{}, 0, pp, pp, sA, sB);  // scores S_1 -> sB
+        __syncthreads();                 // K_1's buffer is refilled by the first pair
+        // pairs (t, t+1) and (t+2, t+3); the last iterations may end a pair early
+        for (int t = 1; t < nkt; t += 4) {
+            pair(Ph1{}, Ph2{}, t);
+            if (t + 2 < nkt) pair(Ph3{}, Ph0{}, t + 2);
         }
-        if (hi == 0) a.lse[split * a.split_lse_stride + (int64_t)bh * a.Sq + qrow] = lse2 * kLn2;
+        // P.V of the last tile
+        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pp, sA, sA, pp, sm);
+
+        // ---- epilogue: normalise, LSE, store (the final output; or, for a stream-K segment, an
+        // fp32 partial and its LSE in the segment's slot)
+        const float l_tot = from_lane(rowsum_partner(lane_it), w.lacc[0]);
+        const float inv_l = 1.f / l_tot;
+        const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
+        if (qrow < ar.Sq) {
+            if (sk_w < 0 && ar.o_bf16) {
+                unsigned short* op = (unsigned short*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * dt + 8 * r4 + 4 * hi_it;
+                        u32x2_t wd;
+                        wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
+                        wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
+                        *(u32x2_t*)(op + d) = wd;
+                    }
+                if (hi_it == 0) ar.lse[(int64_t)bh * ar.Sq + qrow] = lse2 * kLn2;
+            } else {
+                float* op;
+                float* lp;
+                if (sk_w < 0) {
+                    op = (float*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
+                    lp = ar.lse + (int64_t)bh * ar.Sq + qrow;
+                } else {
+                    const int64_t r = (int64_t)(2 * sk_w + seg) * kSkRows + (qrow - qt * C::BQ);
+                    op = ar.sk_o + r * D;
+                    lp = ar.sk_lse + r;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * dt + 8 * r4 + 4 * hi_it;
+                        f32x4_t x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * inv_l;
+                        *(f32x4_t*)(op + d) = x;
+                    }
+                if (hi_it == 0) *lp = lse2 * kLn2;
+            }
+        }
     }
 }
 
@@ -734,8 +798,14 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
         if (dev >= 0 && dev < 64) attr_set[dev] = true;
     }
     const int n_qt = (a.Sq + C::BQ - 1) / C::BQ;
-    if (a.n_split < 1 || (a.n_split > 1 && a.o_bf16)) return hipErrorInvalidValue;
-    const int64_t n_tiles = (int64_t)a.B * a.H * n_qt * a.n_split;
+    const int64_t n_q = (int64_t)a.B * a.H * n_qt;
+    int64_t n_tiles = n_q;
+    if (a.sk_wgs != 0) {
+        // a stream-K tail: every run of its units must stay within two query tiles
+        if (a.n_dp < 0 || a.n_dp >= n_q || a.sk_wgs <= n_q - a.n_dp || !a.sk_o || !a.sk_lse)
+            return hipErrorInvalidValue;
+        n_tiles = (int64_t)a.n_dp + a.sk_wgs;
+    }
     if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
     const float c = (float)((double)a.scale * 1.4426950408889634);
     hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)n_tiles), dim3(C::NT), C::LDS_BYTES, stream, a, n_qt, c);

@@ -31,12 +31,39 @@ struct FwdArgs {
     int n_chunks;        // 1 .. kMaxChunks
     int chunk_row[kMaxChunks];
     int chunk_len[kMaxChunks];  // each > 0
-    // Split over the keys (bf16 path): n_split > 1 launches n_split workgroups per query
-    // tile; split s takes tiles [s*T/n_split, (s+1)*T/n_split) of the T key tiles and writes
-    // an fp32 partial (normalised by its own row sum) and its LSE at o + s*split_o_stride and
-    // lse + s*split_lse_stride (elements); the partials are then merged by their LSE.
-    int n_split;         // 1 = no split
-    int64_t split_o_stride, split_lse_stride;
+    // Balanced tail (bf16 path): sk_wgs > 0 launches n_dp + sk_wgs
+    // workgroups.  Workgroups below n_dp take one whole query tile each (query tiles
+    // 0 .. n_dp-1 of the n_q = B*H*ceil(Sq/kSkRows) in (b, h, tile) order) and write the final
+    // output.  The other query tiles make U = (n_q - n_dp) * T units (query tile, key tile), T
+    // key tiles per query tile; stream-K workgroup w takes units [sk_start(U, w, sk_wgs),
+    // sk_start(U, w + 1, sk_wgs)): at most two query-tile segments, because sk_wgs > n_q - n_dp
+    // makes every range at most T long.  With sk_wgs == 0 the grid is one workgroup per query
+    // tile.  Segment i of workgroup w is written as an fp32 partial
+    // (normalised by its own row sum) with its natural-log LSE into slot 2w + i: row r of the
+    // query tile at sk_o + slot*kSkRows*D + r*D and sk_lse + slot*kSkRows + r.
+    // launch_sk_fixup then merges the partials into the final output.
+    int n_dp;
+    int sk_wgs;          // 0 = no stream-K tail
+    float* sk_o;
+    float* sk_lse;
+};
+
+// Query rows per query tile of the bf16 kernel, and the first unit of stream-K workgroup w.
+constexpr int kSkRows = 256;
+__host__ __device__ inline int64_t sk_start(int64_t U, int w, int n_wgs) { return U * w / n_wgs; }
+
+// Merge of the stream-K partials of query tiles n_dp .. n_q-1 (see FwdArgs).
+struct SkFixupArgs {
+    int B, H, Sq, D;
+    int n_qt;            // query tiles per (b, h): ceil(Sq / kSkRows)
+    int T;               // key tiles per query tile
+    int n_dp, n_q, sk_wgs;
+    const float* sk_o;
+    const float* sk_lse;
+    void* o;             // final output, strides os, bf16 or fp32
+    Strides os;
+    int o_bf16;
+    float* lse;          // [B, H, Sq]
 };
 
 // Merge of up to kMaxMergeParts fp32 partials (contiguous [B,H,Sq,D] / [B,H,Sq]).
@@ -87,6 +114,7 @@ int fp8_key_tiles(int Skv);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_sk_fixup(const SkFixupArgs& a, hipStream_t stream);
 hipError_t launch_fp8_pack_v(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 // O = 0 and LSE = -inf for every row (a chunk without keys).

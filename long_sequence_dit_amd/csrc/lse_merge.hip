@@ -1,4 +1,5 @@
-// Log-sum-exp merge of per-chunk attention results, and the empty-chunk fill.
+// Log-sum-exp merge of per-chunk attention results, the merge of the stream-K tail's partials,
+// and the empty-chunk fill.
 //
 // Results over disjoint key sets combine exactly: with M = max_c LSE_c,
 //   LSE = M + ln sum_c exp(LSE_c - M),   O = sum_c exp(LSE_c - LSE) O_c.
@@ -103,6 +104,57 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     if (d == 0) a.lse[row] = lse_out;
 }
 
+// The stream-K tail of the bf16 kernel (FwdArgs) left, for each query tile j of the tail, fp32
+// partials over consecutive runs of its T key tiles in the slots of the workgroups whose unit
+// ranges meet [jT, (j+1)T).  The first of them is the last workgroup starting at or before jT:
+// w = floor(((jT + 1) P - 1) / U) for P workgroups over U units (ranges may be empty when U < P).
+// A run that starts before jT is its workgroup's second segment.  The runs merge by the LSE rule
+// above; a tile's rows are read and written once.
+__global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
+    const int lanes_per_row = a.D / 4;
+    const int rows_per_block = kThreads / lanes_per_row;
+    const int blocks_per_tile = kSkRows / rows_per_block;
+    const int j = blockIdx.x / blocks_per_tile;
+    const int r = (blockIdx.x % blocks_per_tile) * rows_per_block + threadIdx.x / lanes_per_row;
+    const int d = 4 * (threadIdx.x % lanes_per_row);
+    const int tile = a.n_dp + j;
+    const int bh = tile / a.n_qt, s = (tile % a.n_qt) * kSkRows + r;
+    if (s >= a.Sq) return;
+    const int P = a.sk_wgs;
+    const int64_t U = (int64_t)(a.n_q - a.n_dp) * a.T;
+    const int64_t t0 = (int64_t)j * a.T, t1 = t0 + a.T;
+    const int w0 = (int)(((t0 + 1) * P - 1) / U);
+
+    float M = -INFINITY, tot = 0.f;
+    for (int w = w0; w < P; ++w) {
+        const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
+        if (u0 >= t1) break;
+        if (u1 == u0) continue;
+        const int slot = 2 * w + (u0 < t0 ? 1 : 0);
+        const float l = a.sk_lse[(int64_t)slot * kSkRows + r];
+        if (l == -INFINITY) continue;
+        const float m_new = fmaxf(M, l);
+        tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
+        M = m_new;
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float lse_out = -INFINITY;
+    if (M != -INFINITY) {
+        const float L = M + logf(tot);
+        for (int w = w0; w < P; ++w) {
+            const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
+            if (u0 >= t1) break;
+            if (u1 == u0) continue;
+            const int64_t row = (int64_t)(2 * w + (u0 < t0 ? 1 : 0)) * kSkRows + r;
+            const f32x4_t x = __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d));
+            acc += expf(a.sk_lse[row] - L) * x;
+        }
+        lse_out = L;
+    }
+    store4(a.o, a.os, a.o_bf16, a.H, a.Sq, (int64_t)bh * a.Sq + s, d, acc);
+    if (d == 0) a.lse[(int64_t)bh * a.Sq + s] = lse_out;
+}
+
 __global__ __launch_bounds__(kThreads) void fill_empty_kernel(void* o, Strides os, int o_bf16, float* lse, int H,
                                                               int Sq, int D, int64_t rows) {
     const int lanes_per_row = D / 4;
@@ -131,6 +183,17 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL(merge_kernel<8>, grid, block, 0, stream, a);
     else
         hipLaunchKernelGGL(merge_kernel<16>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sk_fixup(const SkFixupArgs& a, hipStream_t stream) {
+    const int n_tail = a.n_q - a.n_dp;
+    if (n_tail <= 0) return hipSuccess;
+    if ((a.D != 64 && a.D != 128) || a.sk_wgs <= 0 || a.T <= 0) return hipErrorInvalidValue;
+    const int blocks_per_tile = kSkRows / (kThreads / (a.D / 4));
+    const int64_t blocks = (int64_t)n_tail * blocks_per_tile;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sk_fixup_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -151,13 +151,16 @@ def test_workspace_sizes(attn):
     slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot   # n-way
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 2 * slot   # online
-    # fused: no chunk partials; a shape with few query tiles (16 heads x 22 tiles of 256 rows,
-    # fewer than the GPU's CUs can run in full rounds) gets room to split its key range over
-    # 2..8 workgroups per query tile, a shape with many query tiles none
-    ws = lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4)
-    assert ws % slot == 0 and 2 <= ws // slot <= 8, ws / slot
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == ws  # one chunk: same kernel
-    assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == 0
+    # fused: no chunk partials.  A shape whose query tiles of 256 rows leave the last round of
+    # the GPU's CUs part-full (16 heads x 22 tiles = 352 on 256 CUs; the CPU build assumes 256)
+    # gets room for the balanced tail: 2 slots of 256 rows x (D + 1) fp32 per CU, whatever the
+    # chunking; a shape filling whole rounds (16 x 16 tiles) none
+    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == tail
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == tail  # one chunk: same kernel
+    assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == tail  # 2768 tiles: 208 in the last round
+    assert lib.attn_shard_workspace_size(1, 16, 4096, 128, 8, 4) == 0
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 64, 8, 4) == 2 * 256 * 256 * 64 * 4 + 2 * 256 * 256 * 4
     assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0
 

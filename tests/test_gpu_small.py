@@ -122,21 +122,48 @@ def test_max_chunks_random_lengths_and_order(dtype, mode):
 
 
 @pytest.mark.parametrize("D", [128, 64])
-@pytest.mark.parametrize("Skv", [260, 512, 3000])
-def test_key_split_matches_unsplit(Skv, D):
-    """Few query tiles: the fused schedule splits the key tiles over several workgroups per
-    query tile when given the workspace (and runs unsplit without it); both match the oracle."""
+@pytest.mark.parametrize("Skv", [5000, 9000])
+def test_balanced_tail_few_query_tiles(Skv, D):
+    """Three query tiles against 79 or 141 key tiles: with the workspace, the fused schedule
+    spreads the work over the CUs as runs of about one key tile (the fix-up then merges some 80
+    partials per row); without it, one workgroup per query tile.  Both match the oracle."""
     B, H, Sq = 1, 3, 200
     q, k, v = _inputs(B, H, Sq, Skv, D, seed=21)
     o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     lens = (Skv // 3, Skv - Skv // 3)
     need = A().shard_workspace_size(B, H, Sq, D, len(lens), "fused")
-    assert need > 0  # 3 query tiles: room for a split
+    assert need > 0  # 3 query tiles leave the last round part-full
     for ws in (torch.empty(need, dtype=torch.uint8, device="cuda"), torch.empty(0, dtype=torch.uint8, device="cuda")):
         o, l = A().shard_fwd(qd, kd, vd, lens, (1, 0), mode="fused", workspace=ws)
         torch.cuda.synchronize()
         assert_parity(o, l, o_ref, l_ref, what="Skv %d workspace %d" % (Skv, ws.numel()))
+
+
+def test_balanced_tail_spans_query_tiles():
+    """300 query tiles (20 heads x 15, the last of each head 16 rows) against 79 key tiles in two
+    chunks: 256 run whole, and the 44 of the tail as 256 runs of 13-14 key tiles, many crossing
+    from one query tile into the next.  Rows of whole tiles, of tail tiles (first, crossing,
+    last) and of the ragged last tiles match the oracle; the result also matches the run
+    without the tail."""
+    B, H, Sq, Skv, D = 1, 20, 3600, 5000, 128
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=23)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    lens, order = (2000, 3000), (1, 0)
+    need = A().shard_workspace_size(B, H, Sq, D, 2, "fused")
+    assert need > 0
+    o, l = A().shard_fwd(qd, kd, vd, lens, order, mode="fused",
+                         workspace=torch.empty(need, dtype=torch.uint8, device="cuda"))
+    o_dp, l_dp = A().shard_fwd(qd, kd, vd, lens, order, mode="fused",
+                               workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    # query tile t of the 15 per head: head t // 15, rows 256 (t % 15) ..; tiles 256.. are the tail
+    rows = sorted({0, 255, 256, 3583, 3584, 3599} | set(range(0, Sq, 97)))
+    for h in (0, 17, 19):  # whole tiles only; tail from tile 256 (head 17, tile 1); tail only
+        o_ref, l_ref = oracle.attention(q[:, h:h + 1, rows], k[:, h:h + 1], v[:, h:h + 1], 1 / math.sqrt(D))
+        assert_parity(o[:, h:h + 1, rows], l[:, h:h + 1, rows], o_ref, l_ref, what="tail spans, head %d" % h)
+    assert float((o.float() - o_dp.float()).abs().max()) <= 2e-2
+    assert float((l - l_dp).abs().max()) <= 1e-3
 
 
 @pytest.mark.parametrize("D", [128, 64])
