@@ -212,10 +212,13 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
  *   D        128 only (else ATTN_ERR_UNSUPPORTED)
  *   o, lse   as attn_chunk_fwd: O in o_dt (ATTN_BF16 or ATTN_F32), natural-log
  *            LSE fp32 [B,H,Sq] contiguous, scale included
- *   workspace  device scratch of at least attn_fp8_workspace_size(B,H,Skv,D)
+ *   workspace  device scratch of at least attn_fp8_workspace_size(B,H,Sq,Skv,D)
  *            bytes, 16-byte aligned, owned by the caller; it receives V
- *            re-laid out as transposed 64-key tiles and may be reused once the
- *            call's work on `stream` has finished
+ *            re-laid out as transposed 64-key tiles and, when the query tiles
+ *            (256 rows) leave the last round of CUs part-full and the keys
+ *            are many, the fp32 partials of the balanced tail (as in
+ *            attn_shard_fwd); it may be reused once the call's work on
+ *            `stream` has finished
  * The probabilities enter P.V as E4M3 (after scaling by 2^5), so the result
  * differs from exact attention of the decoded inputs by up to 2^-4 of the
  * probability-weighted mean of |V| per element (relative rounding of each
@@ -225,7 +228,7 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
  * (ATTN_ERR_UNSUPPORTED); a short workspace gives ATTN_ERR_WORKSPACE.
  * Sq = 0, B = 0 or H = 0 is a no-op; Skv = 0 gives O = 0, LSE = -inf.
  */
-size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Skv, int32_t D);
+size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t Skv, int32_t D);
 attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
                                  attn_strides_t vs, float q_descale, float k_descale, float v_descale, int32_t B,
                                  int32_t H, int32_t Sq, int32_t Skv, int32_t D, float scale, void* workspace,

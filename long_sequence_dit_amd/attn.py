@@ -73,7 +73,7 @@ def load():
         lib.attn_ulysses_pack.restype = ctypes.c_int
         lib.attn_ulysses_unpack.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, i32, vp, Strides, vp]
         lib.attn_ulysses_unpack.restype = ctypes.c_int
-        lib.attn_fp8_workspace_size.argtypes = [i32, i32, i32, i32]
+        lib.attn_fp8_workspace_size.argtypes = [i32, i32, i32, i32, i32]
         lib.attn_fp8_workspace_size.restype = sz
         lib.attn_chunk_fwd_fp8.argtypes = [vp, Strides, vp, Strides, vp, Strides, f32, f32, f32, i32, i32, i32, i32,
                                            i32, f32, vp, sz, vp, Strides, ctypes.c_int, vp, vp]
@@ -148,8 +148,8 @@ def chunk_fwd(q, k, v, scale=None, out=None, lse=None, out_dtype=None, stream=No
     return out, lse
 
 
-def fp8_workspace_size(B, H, Skv, D) -> int:
-    return int(load().attn_fp8_workspace_size(B, H, Skv, D))
+def fp8_workspace_size(B, H, Sq, Skv, D) -> int:
+    return int(load().attn_fp8_workspace_size(B, H, Sq, Skv, D))
 
 
 def _e4m3(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -175,7 +175,7 @@ def chunk_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise ValueError("lse must be contiguous fp32 [B, H, Sq]")
-    need = fp8_workspace_size(B, H, Skv, D)
+    need = fp8_workspace_size(B, H, Sq, Skv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     rc = load().attn_chunk_fwd_fp8(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),

@@ -358,9 +358,20 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
     return relayout(packed, x, xs, dt, B, H, S, D, n, false, (hipStream_t)stream);
 }
 
-size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Skv, int32_t D) {
-    if (B <= 0 || H <= 0 || Skv <= 0 || D != 128) return 0;
+namespace {
+// The FP8 call's workspace: V^T tiles, then the balanced tail's partials when it runs.
+size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
     return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
+}
+SkPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
+    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus());
+}
+}  // namespace
+
+size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t Skv, int32_t D) {
+    if (B <= 0 || H <= 0 || Sq < 0 || Skv <= 0 || D != 128) return 0;
+    const SkPlan p = fp8_plan(B, H, Sq, Skv);
+    return fp8_vt_bytes(B, H, Skv) + (p.sk_wgs ? sk_bytes(p.sk_wgs, D) : 0);
 }
 
 attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
@@ -388,7 +399,7 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     // 32-bit buffer offsets: one head's K rows and V^T tiles, plus the four tiles the kernel
     // fetches past the end
     if ((int64_t)(Skv + 320) * ks.s >= ((int64_t)1 << 31) || Skv >= (1 << 23)) return ATTN_ERR_UNSUPPORTED;
-    if (ws_bytes < attn_fp8_workspace_size(B, H, Skv, D)) return ATTN_ERR_WORKSPACE;
+    if (ws_bytes < attn_fp8_workspace_size(B, H, Sq, Skv, D)) return ATTN_ERR_WORKSPACE;
     lsdit::Fp8Args a{};
     a.q = q; a.k = k; a.v = v;
     a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
@@ -399,8 +410,25 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     a.c = (float)((double)scale * 1.4426950408889634 * (double)q_descale * (double)k_descale);
     a.v_descale = v_descale;
     if (!(a.c > 0.f) || !isfinite(a.c)) return ATTN_ERR_SHAPE;
+    // the balanced tail, as in attn_shard_fwd, its partials after V^T in the workspace
+    const SkPlan p = fp8_plan(B, H, Sq, Skv);
+    if (p.sk_wgs) {
+        a.n_dp = p.n_dp;
+        a.sk_wgs = p.sk_wgs;
+        a.sk_o = (float*)((char*)workspace + fp8_vt_bytes(B, H, Skv));
+        a.sk_lse = (float*)((char*)a.sk_o + sk_o_bytes(p.sk_wgs, D));
+    }
     if (lsdit::launch_fp8_pack_v(a, s) != hipSuccess) return ATTN_ERR_HIP;
-    return lsdit::launch_fwd_fp8(a, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    if (lsdit::launch_fwd_fp8(a, s) != hipSuccess) return ATTN_ERR_HIP;
+    if (!p.sk_wgs) return ATTN_OK;
+    lsdit::SkFixupArgs f{};
+    f.B = B; f.H = H; f.Sq = Sq; f.D = D;
+    f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
+    f.T = lsdit::fp8_key_tiles(Skv);
+    f.n_dp = p.n_dp; f.n_q = (int)n_qtiles(B, H, Sq); f.sk_wgs = p.sk_wgs;
+    f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
+    f.o = o; f.os = S(os); f.o_bf16 = o_dt == ATTN_BF16; f.lse = lse;
+    return lsdit::launch_sk_fixup(f, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 const char* attn_status_str(attn_status_t s) {

@@ -52,6 +52,9 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+// Kernel arguments seen through the constant address space (scalar loads).
+template <class T>
+using kernarg_t = __attribute__((address_space(4))) const T;
 
 constexpr int D = 128;
 constexpr int NW = 8;               // waves per workgroup
@@ -321,7 +324,6 @@ __device__ __forceinline__ void stream_slots(Wave& w, const Addr& ad, unsigned v
                                              i32x8_t (&ring)[kPrefetch], const i32x8_t& p_prev,
                                              const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], i32x8_t& p_cur,
                                              Soft& sm) {
-    constexpr int first = DO_PV ? 0 : N_PV;
     constexpr int last = DO_S ? N_SLOTS : N_PV;
     if constexpr (SLOT < last) {
         if constexpr (SLOT < 4) {
@@ -374,218 +376,269 @@ __device__ __forceinline__ void stream(Wave& w, const Addr& ad, unsigned v0, uns
 __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int n_kt) {
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     (void)smem;  // no static LDS: the dynamic block starts at LDS address 0
+    static_assert(BQ == kSkRows, "stream-K slots hold one query tile");
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hi = lane >> 5;
-    const int gidx = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = gidx / n_qt, qt = gidx % n_qt;
-    const int b = bh / a.H, h = bh % a.H;
+    const int n_q = a.B * a.H * n_qt;
 
-    const unsigned char* qp = (const unsigned char*)a.q + b * a.qs.b + h * a.qs.h;
-    const unsigned char* kp = (const unsigned char*)a.k + b * a.ks.b + h * a.ks.h;
-    const int Skv = a.Skv;
-    const int nkt = n_kt;
-
-    Wave w;
-    w.c = a.c;
-    w.m_run = -INFINITY;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
-    w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    {
-        const int ra = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? (int)kOnes : 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) w.rs_a[r] = ra;
-    }
-    asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
-
-    // Q bytes: lane (row, half h) holds d = 64 kk + 32 h .. +32 of its row
-    const int qrow = qt * BQ + wave * 32 + (lane & 31);
-    const int qrow_c = qrow < a.Sq ? qrow : a.Sq - 1;
-#pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) {
-        const u32x4_t* src = (const u32x4_t*)(qp + (int64_t)qrow_c * a.qs.s + 64 * kk + 32 * hi);
-        const u32x4_t lo = src[0], hi4 = src[1];
-        w.qf[kk] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                           (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-    }
-
-    // tile loads: K rows through a per-lane swizzled offset, V^T tiles verbatim
-    const int k_rs = (int)a.ks.s;  // bytes per K row step
-    const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D);
-    const Rsrc vrs = make_rsrc((const unsigned char*)a.vt + (int64_t)bh * nkt * TILE, nkt * TILE);
-    int k_goff[BLKS_PER_WAVE], v_goff[BLKS_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-        const int blk = wave * BLKS_PER_WAVE + i;
-        const int row = blk * 8 + lane / 8, slot = lane % 8;
-        k_goff[i] = row * k_rs + (slot ^ k_swz(row)) * 16;
-        v_goff[i] = blk * 1024 + lane * 16;
-    }
-    // LDS byte offsets of the tile buffers: tile g of K and V sits in buffer g mod NSTAGE
-    auto kbuf = [&](int t) { return (unsigned)((t % NSTAGE) * TILE); };
-    auto vbuf = [&](int t) { return (unsigned)((NSTAGE + t % NSTAGE) * TILE); };
-    auto load_k = [&](int g) {
-        if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(krs, kbuf(g) + wave * BLKS_PER_WAVE * 1024, k_goff, g * BK * k_rs);
-    };
-    auto load_v = [&](int g) {
-        if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(vrs, vbuf(g) + wave * BLKS_PER_WAVE * 1024, v_goff, g * TILE);
-    };
-
-    // per-lane operand offsets
-    Addr ad;
-    {
-        const int l32 = lane & 31;
-        ad.va[0] = l32 * 64 + (((2 * hi) ^ vt_swz(l32)) * 16);
-        ad.va[1] = l32 * 64 + (((2 * hi + 1) ^ vt_swz(l32)) * 16);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) ad.ka[kk][j] = l32 * K_ROW + (((4 * kk + 2 * hi + j) ^ k_swz(l32)) * 16);
-        // opaque to the compiler, so that buffer and block offsets stay additions it folds into
-        // the reads' offset fields (with the offsets' bits known disjoint it may turn them
-        // into ORs computed per read)
-        asm volatile("" : "+v"(ad.va[0]), "+v"(ad.va[1]), "+v"(ad.ka[0][0]), "+v"(ad.ka[0][1]), "+v"(ad.ka[1][0]),
-                     "+v"(ad.ka[1][1]));
-    }
-
-    // scores of keys at or past `valid` in a tile -> -inf (key of element (kb, r) is
-    // 32 kb + 8 (r >> 2) + 4 hi + (r & 3))
-    auto mask = [&](f32x16_t(&s)[2], int valid) {
-        if (valid < BK) {
-            const int lim = valid - 4 * hi;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
-        }
-    };
-    auto valid_of = [&](int t) { return Skv - t * BK; };
-
-    // prologue: zero the buffers (rows past the end are masked; zeros keep 0 * V finite)
-    for (int i = tid; i < LDS_BYTES / 16; i += NT) *(lds_u32x4_t*)(size_t)(16u * i) = u32x4_t{0u, 0u, 0u, 0u};
-    __syncthreads();
-    // every K buffer, and the V tiles of the first pair of iterations (see below)
-#pragma unroll
-    for (int g = 0; g < NSTAGE; ++g) load_k(g);
-#pragma unroll
-    for (int g = 0; g < NSTAGE / 2; ++g) load_v(g);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-
-    f32x16_t sA[2], sB[2];
-    i32x8_t pA = {}, pB = {};
-    Soft sm;
-    auto finish_softmax = [&]() {
-        if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
-            // only element 0 of the row sums is read; the others may drift.  The lane's row sum
-            // belongs to its partner's query, so it takes the partner's factor.
-            w.lacc[0] *= from_lane(rowsum_partner(lane), sm.alpha);
-        }
-    };
-    stream<false, true, false>(w, ad, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
-    mask(sA, valid_of(0));
-    softmax_all(w, sm, sA, pA);  // P_0 -> pA
-    finish_softmax();
-    __syncthreads();
-
-    // Iteration t: P.V of tile t-1 (V_{t-1}), the softmax of tile t, the scores of tile t+1
-    // (K_{t+1}).  With P = t mod NSTAGE a compile-time constant, the buffers it reads are
-    // constants, which fold into the LDS reads' offset fields.
-    // (always inlined: as calls, the register arrays they touch would go to scratch)
-    auto body = [&](auto phase, int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2],
-                    f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
-        constexpr int P = decltype(phase)::value;
-        constexpr unsigned k_next = ((P + 1) % NSTAGE) * TILE;                     // K_{t+1}
-        constexpr unsigned v_prev = (NSTAGE + (P + NSTAGE - 1) % NSTAGE) * TILE;  // V_{t-1}
-        if (t == 0) {
-            stream<false, true, false>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+    // This workgroup's segments (query tile, run of key tiles): one whole query tile, or, for a
+    // workgroup of the balanced tail (see Fp8Args), its run of (query tile, key tile) units,
+    // which spans at most two query tiles.  As in the bf16 kernel, each iteration re-derives its
+    // segment, the arguments (through an opaque pointer) and the lane index, so nothing computed
+    // from them is held across the key loop, and the segment bounds are made wave-uniform.
+    for (int seg = 0;; ++seg) {
+        const kernarg_t<Fp8Args>* ap = (const kernarg_t<Fp8Args>*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        const kernarg_t<Fp8Args>& ar = *ap;
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int hi = lane >> 5;
+        int sk_w = -1, gidx, g_first, nkt;
+        if (ar.sk_wgs == 0 || (int)blockIdx.x < ar.n_dp) {
+            if (seg > 0) break;
+            gidx = xcd_remap(blockIdx.x, ar.sk_wgs == 0 ? n_q : ar.n_dp);
+            g_first = 0;
+            nkt = n_kt;
         } else {
-            stream<true, true, true>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
-            finish_softmax();
+            sk_w = xcd_remap(blockIdx.x - ar.n_dp, ar.sk_wgs);
+            const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
+            const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
+            const int64_t cut = (u0 / n_kt + 1) * n_kt;
+            const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
+            if (seg > 1 || s0 >= s1) break;
+            gidx = ar.n_dp + (int)(s0 / n_kt);
+            g_first = (int)(s0 % n_kt);
+            nkt = (int)(s1 - s0);
         }
-        if (t + 1 < nkt) mask(s_next, valid_of(t + 1));
-    };
-    // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
-    // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
-    // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
-    // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
-    // they wait for those loads, and the barrier publishes them.
-    static_assert(NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
-    auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
-        load_k(t + 3);
-        load_k(t + 4);
-        load_v(t + 1);
-        load_v(t + 2);
-        body(ph0, t, pA, pB, sB, sA);                 // odd t: P_{t-1} in pA, S_t in sB
-        if (t + 1 < nkt) body(ph1, t + 1, pB, pA, sA, sB);
+        gidx = __builtin_amdgcn_readfirstlane(gidx);
+        g_first = __builtin_amdgcn_readfirstlane(g_first);
+        nkt = __builtin_amdgcn_readfirstlane(nkt);
+        sk_w = __builtin_amdgcn_readfirstlane(sk_w);
+        if (seg > 0) {
+            // every wave is done with the previous segment's tiles (and no load is in flight)
+            // before this segment's prologue rewrites LDS
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+        }
+        const int bh = gidx / n_qt, qt = gidx % n_qt;
+        const int b = bh / ar.H, h = bh % ar.H;
+        const unsigned char* qp = (const unsigned char*)ar.q + b * ar.qs.b + h * ar.qs.h;
+        const unsigned char* kp = (const unsigned char*)ar.k + b * ar.ks.b + h * ar.ks.h;
+        const int Skv = ar.Skv;
+
+        Wave w;
+        w.c = ar.c;
+        w.m_run = -INFINITY;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.acc[dt][r] = 0.f;
+        w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            const int ra = ((lane >> 4) & 1) == ((lane & 15) >> 3) ? (int)kOnes : 0;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) w.rs_a[r] = ra;
+        }
+        asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
+
+        // Q bytes: lane (row, half h) holds d = 64 kk + 32 h .. +32 of its row
+        const int qrow = qt * BQ + wave * 32 + (lane & 31);
+        const int qrow_c = qrow < ar.Sq ? qrow : ar.Sq - 1;
+#pragma unroll
+        for (int kk = 0; kk < D / 64; ++kk) {
+            const u32x4_t* src = (const u32x4_t*)(qp + (int64_t)qrow_c * ar.qs.s + 64 * kk + 32 * hi);
+            const u32x4_t lo = src[0], hi4 = src[1];
+            w.qf[kk] = i32x8_t{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                               (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+        }
+
+        // tile loads: K rows through a per-lane swizzled offset, V^T tiles verbatim
+        const int k_rs = (int)ar.ks.s;  // bytes per K row step
+        const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D);
+        const Rsrc vrs = make_rsrc((const unsigned char*)ar.vt + (int64_t)bh * n_kt * TILE, n_kt * TILE);
+        int k_goff[BLKS_PER_WAVE], v_goff[BLKS_PER_WAVE];
+#pragma unroll
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            const int blk = wave * BLKS_PER_WAVE + i;
+            const int row = blk * 8 + lane / 8, slot = lane % 8;
+            k_goff[i] = row * k_rs + (slot ^ k_swz(row)) * 16;
+            v_goff[i] = blk * 1024 + lane * 16;
+        }
+        // LDS byte offsets of the tile buffers: tile g of the segment (key tile g_first + g) sits in
+        // buffer g mod NSTAGE
+        auto kbuf = [&](int t) { return (unsigned)((t % NSTAGE) * TILE); };
+        auto vbuf = [&](int t) { return (unsigned)((NSTAGE + t % NSTAGE) * TILE); };
+        auto load_k = [&](int g) {
+            if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(krs, kbuf(g) + wave * BLKS_PER_WAVE * 1024, k_goff, (g_first + g) * BK * k_rs);
+        };
+        auto load_v = [&](int g) {
+            if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(vrs, vbuf(g) + wave * BLKS_PER_WAVE * 1024, v_goff, (g_first + g) * TILE);
+        };
+
+        // per-lane operand offsets
+        Addr ad;
+        {
+            const int l32 = lane & 31;
+            ad.va[0] = l32 * 64 + (((2 * hi) ^ vt_swz(l32)) * 16);
+            ad.va[1] = l32 * 64 + (((2 * hi + 1) ^ vt_swz(l32)) * 16);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) ad.ka[kk][j] = l32 * K_ROW + (((4 * kk + 2 * hi + j) ^ k_swz(l32)) * 16);
+            // opaque to the compiler, so that buffer and block offsets stay additions it folds into
+            // the reads' offset fields (with the offsets' bits known disjoint it may turn them
+            // into ORs computed per read)
+            asm volatile("" : "+v"(ad.va[0]), "+v"(ad.va[1]), "+v"(ad.ka[0][0]), "+v"(ad.ka[0][1]), "+v"(ad.ka[1][0]),
+                         "+v"(ad.ka[1][1]));
+        }
+
+        // scores of keys at or past `valid` in a tile -> -inf (key of element (kb, r) is
+        // 32 kb + 8 (r >> 2) + 4 hi + (r & 3))
+        auto mask = [&](f32x16_t(&s)[2], int valid) {
+            if (valid < BK) {
+                const int lim = valid - 4 * hi;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+            }
+        };
+        auto valid_of = [&](int t) { return Skv - (g_first + t) * BK; };
+
+        // prologue: zero the buffers (rows past the end are masked; zeros keep 0 * V finite)
+        for (int i = tid; i < LDS_BYTES / 16; i += NT) *(lds_u32x4_t*)(size_t)(16u * i) = u32x4_t{0u, 0u, 0u, 0u};
+        __syncthreads();
+        // every K buffer, and the V tiles of the first pair of iterations (see below)
+#pragma unroll
+        for (int g = 0; g < NSTAGE; ++g) load_k(g);
+#pragma unroll
+        for (int g = 0; g < NSTAGE / 2; ++g) load_v(g);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-    };
-    using Ph0 = std::integral_constant<int, 0>;
-    using Ph1 = std::integral_constant<int, 1>;
-    using Ph2 = std::integral_constant<int, 2>;
-    using Ph3 = std::integral_constant<int, 3>;
-    body(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
-    __syncthreads();                 // K_1's buffer is refilled by the first pair
-    int t = 1;
-    for (; t + 3 < nkt; t += 4) {
-        pair(Ph1{}, Ph2{}, t);
-        pair(Ph3{}, Ph0{}, t + 2);
-    }
-    // t = 1 mod 4 here: at most three more iterations
-    if (t < nkt) {
-        pair(Ph1{}, Ph2{}, t);
-        t += 2;
-    }
-    if (t < nkt) {
-        pair(Ph3{}, Ph0{}, t);
-        t += 2;
-    }
-    if (nkt & 1)
-        stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
-    else
-        stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
 
-    // epilogue: O = acc * v_descale / l, LSE = ln2 (m + log2 l - kPShift)
-    const float l_tot = from_lane(rowsum_partner(lane), w.lacc[0]);
-    const float inv_l = a.v_descale / l_tot;
-    const float lse2 = w.m_run + log2f(l_tot) - kPShift;
-    if (qrow < a.Sq) {
-        if (a.o_bf16) {
-            unsigned short* op = (unsigned short*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
+        f32x16_t sA[2], sB[2];
+        i32x8_t pA = {}, pB = {};
+        Soft sm;
+        auto finish_softmax = [&]() {
+            if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * dt + 8 * r4 + 4 * hi;
-                    u32x2_t wd;
-                    wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
-                    wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
-                    *(u32x2_t*)(op + d) = wd;
-                }
-        } else {
-            float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int d = 32 * dt + 8 * r4 + 4 * hi;
-                    *(u32x4_t*)(op + d) = u32x4_t{__float_as_uint(w.acc[dt][4 * r4] * inv_l),
-                                                  __float_as_uint(w.acc[dt][4 * r4 + 1] * inv_l),
-                                                  __float_as_uint(w.acc[dt][4 * r4 + 2] * inv_l),
-                                                  __float_as_uint(w.acc[dt][4 * r4 + 3] * inv_l)};
-                }
+                    for (int r = 0; r < 16; ++r) w.acc[dt][r] *= sm.alpha;
+                // only element 0 of the row sums is read; the others may drift.  The lane's row sum
+                // belongs to its partner's query, so it takes the partner's factor.
+                w.lacc[0] *= from_lane(rowsum_partner(lane), sm.alpha);
+            }
+        };
+        stream<false, true, false>(w, ad, vbuf(0), kbuf(0), pB, sA, sA, pB, sm);  // S_0 -> sA
+        mask(sA, valid_of(0));
+        softmax_all(w, sm, sA, pA);  // P_0 -> pA
+        finish_softmax();
+        __syncthreads();
+
+        // Iteration t: P.V of tile t-1 (V_{t-1}), the softmax of tile t, the scores of tile t+1
+        // (K_{t+1}).  With P = t mod NSTAGE a compile-time constant, the buffers it reads are
+        // constants, which fold into the LDS reads' offset fields.
+        // (always inlined: as calls, the register arrays they touch would go to scratch)
+        auto body = [&](auto phase, int t, i32x8_t& p_prev, i32x8_t& p_cur, f32x16_t(&s_cur)[2],
+                        f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
+            constexpr int P = decltype(phase)::value;
+            constexpr unsigned k_next = ((P + 1) % NSTAGE) * TILE;                     // K_{t+1}
+            constexpr unsigned v_prev = (NSTAGE + (P + NSTAGE - 1) % NSTAGE) * TILE;  // V_{t-1}
+            if (t == 0) {
+                stream<false, true, false>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+            } else {
+                stream<true, true, true>(w, ad, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+                finish_softmax();
+            }
+            if (t + 1 < nkt) mask(s_next, valid_of(t + 1));
+        };
+        // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
+        // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
+        // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
+        // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
+        // they wait for those loads, and the barrier publishes them.
+        static_assert(NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
+        auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
+            load_k(t + 3);
+            load_k(t + 4);
+            load_v(t + 1);
+            load_v(t + 2);
+            body(ph0, t, pA, pB, sB, sA);                 // odd t: P_{t-1} in pA, S_t in sB
+            if (t + 1 < nkt) body(ph1, t + 1, pB, pA, sA, sB);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            __syncthreads();
+        };
+        using Ph0 = std::integral_constant<int, 0>;
+        using Ph1 = std::integral_constant<int, 1>;
+        using Ph2 = std::integral_constant<int, 2>;
+        using Ph3 = std::integral_constant<int, 3>;
+        body(Ph0{}, 0, pB, pA, sA, sB);  // scores S_1 -> sB
+        __syncthreads();                 // K_1's buffer is refilled by the first pair
+        int t = 1;
+        for (; t + 3 < nkt; t += 4) {
+            pair(Ph1{}, Ph2{}, t);
+            pair(Ph3{}, Ph0{}, t + 2);
         }
-        if (hi == 0) a.lse[((int64_t)b * a.H + h) * a.Sq + qrow] = lse2 * kLn2;
+        // t = 1 mod 4 here: at most three more iterations
+        if (t < nkt) {
+            pair(Ph1{}, Ph2{}, t);
+            t += 2;
+        }
+        if (t < nkt) {
+            pair(Ph3{}, Ph0{}, t);
+            t += 2;
+        }
+        if (nkt & 1)
+            stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pA, sA, sA, pB, sm);
+        else
+            stream<true, false, false>(w, ad, vbuf(nkt - 1), kbuf(0), pB, sA, sA, pA, sm);
+
+        // epilogue: O = acc * v_descale / l, LSE = ln2 (m + log2 l - kPShift)
+        const float l_tot = from_lane(rowsum_partner(lane), w.lacc[0]);
+        const float inv_l = ar.v_descale / l_tot;
+        const float lse2 = w.m_run + log2f(l_tot) - kPShift;
+        if (qrow < ar.Sq) {
+            if (sk_w < 0 && ar.o_bf16) {
+                unsigned short* op = (unsigned short*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * dt + 8 * r4 + 4 * hi;
+                        u32x2_t wd;
+                        wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
+                        wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
+                        *(u32x2_t*)(op + d) = wd;
+                    }
+                if (hi == 0) ar.lse[(int64_t)bh * ar.Sq + qrow] = lse2 * kLn2;
+            } else {
+                // the final fp32 output, or a tail segment's fp32 partial and LSE in its slot
+                float* op;
+                float* lp;
+                if (sk_w < 0) {
+                    op = (float*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
+                    lp = ar.lse + (int64_t)bh * ar.Sq + qrow;
+                } else {
+                    const int64_t r = (int64_t)(2 * sk_w + seg) * kSkRows + (qrow - qt * BQ);
+                    op = ar.sk_o + r * D;
+                    lp = ar.sk_lse + r;
+                }
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const int d = 32 * dt + 8 * r4 + 4 * hi;
+                        *(u32x4_t*)(op + d) = u32x4_t{__float_as_uint(w.acc[dt][4 * r4] * inv_l),
+                                                      __float_as_uint(w.acc[dt][4 * r4 + 1] * inv_l),
+                                                      __float_as_uint(w.acc[dt][4 * r4 + 2] * inv_l),
+                                                      __float_as_uint(w.acc[dt][4 * r4 + 3] * inv_l)};
+                    }
+                if (hi == 0) *lp = lse2 * kLn2;
+            }
+        }
     }
 }
 
@@ -605,8 +658,15 @@ hipError_t launch_fp8_pack_v(const Fp8Args& a, hipStream_t stream) {
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
     const int n_qt = (a.Sq + BQ - 1) / BQ;
     const int n_kt = fp8_key_tiles(a.Skv);
-    const int64_t blocks = (int64_t)a.B * a.H * n_qt;
-    if (blocks <= 0 || n_kt <= 0) return hipSuccess;
+    const int64_t n_q = (int64_t)a.B * a.H * n_qt;
+    if (n_q <= 0 || n_kt <= 0) return hipSuccess;
+    int64_t blocks = n_q;
+    if (a.sk_wgs != 0) {
+        // a stream-K tail: every run of its units must stay within two query tiles
+        if (a.n_dp < 0 || a.n_dp >= n_q || a.sk_wgs <= n_q - a.n_dp || !a.sk_o || !a.sk_lse)
+            return hipErrorInvalidValue;
+        blocks = (int64_t)a.n_dp + a.sk_wgs;
+    }
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
     static bool attr_set[64] = {};
     int dev = 0;

@@ -107,6 +107,11 @@ struct Fp8Args {
     int B, H, Sq, Skv;   // Skv >= 1
     float c;             // scale * log2(e) * q_descale * k_descale
     float v_descale;
+    // Balanced tail, as in FwdArgs (query tiles of kSkRows rows, T = fp8_key_tiles(Skv))
+    int n_dp;
+    int sk_wgs;          // 0 = no stream-K tail
+    float* sk_o;
+    float* sk_lse;
 };
 int fp8_key_tiles(int Skv);
 

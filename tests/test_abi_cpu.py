@@ -186,10 +186,16 @@ def test_ulysses_relayout_argument_errors(attn):
 def test_fp8_argument_errors(attn):
     lib = attn.load()
     c = _st(2 * 1000 * 128, 1000 * 128, 128)
-    need = lib.attn_fp8_workspace_size(1, 2, 20, 128)
-    assert need == 1 * 2 * 1 * 8192
-    assert lib.attn_fp8_workspace_size(1, 2, 65, 128) == 2 * 2 * 8192
-    assert lib.attn_fp8_workspace_size(1, 2, 20, 64) == 0 and lib.attn_fp8_workspace_size(1, 2, 0, 128) == 0
+    need = lib.attn_fp8_workspace_size(1, 2, 10, 20, 128)
+    assert need == 1 * 2 * 1 * 8192          # V^T tiles of 64 keys; no tail for 2 query tiles of 1 key tile
+    assert lib.attn_fp8_workspace_size(1, 2, 10, 65, 128) == 2 * 2 * 8192
+    assert lib.attn_fp8_workspace_size(1, 2, 10, 20, 64) == 0 and lib.attn_fp8_workspace_size(1, 2, 10, 0, 128) == 0
+    # 16 heads x 173 query tiles against 690 key tiles leave 208 tiles in the last round of 256 CUs
+    # (the CPU build assumes 256): room for the balanced tail after V^T; 16 x 16 tiles fill it
+    vt = 16 * 690 * 8192
+    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4
+    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + tail
+    assert lib.attn_fp8_workspace_size(1, 16, 4096, 44160, 128) == vt
 
     def f(q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=need, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1, dq=1.0, dk=1.0,
           dv=1.0, odt=BF16, qs=None, ks=None, vs=None, os_=None):

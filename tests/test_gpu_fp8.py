@@ -150,7 +150,7 @@ def test_fp8_uniform_values_and_descale_algebra():
 
 def test_fp8_deterministic_workspace_reuse_and_empty():
     inp = _quantized(1, 2, 300, 900, seed=6)
-    ws = torch.empty(A().fp8_workspace_size(1, 2, 900, 128) + 4096, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(A().fp8_workspace_size(1, 2, 300, 900, 128) + 4096, dtype=torch.uint8, device="cuda")
     o1, l1 = _run(inp, 0.1, workspace=ws)
     small = _quantized(1, 2, 300, 100, seed=7)
     _run(small, 0.1, workspace=ws)  # the same workspace, different contents in between
@@ -162,6 +162,17 @@ def test_fp8_deterministic_workspace_reuse_and_empty():
     o, l = A().chunk_fwd_fp8(q, e, e, 1.0, 1.0, 1.0, 0.1)
     torch.cuda.synchronize()
     assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+
+
+def test_fp8_balanced_tail():
+    """Three query tiles against 79 key tiles: the work is spread over 237 workgroups of one key
+    tile each, whose fp32 partials the fix-up merges (79 per row).  Within a run the lazy
+    reference is the run's own, so every probability is rounded at least as finely as in one
+    pass, and the merge normalises by the sum of the rounded probabilities: the bound holds."""
+    inp = _quantized(1, 3, 200, 5000, seed=8)
+    assert A().fp8_workspace_size(1, 3, 200, 5000, 128) > 3 * 79 * 8192  # V^T and the tail's slots
+    o, l = _run(inp, 1 / math.sqrt(128))
+    check_fp8(o, l, inp, 1 / math.sqrt(128), what="fp8 balanced tail")
 
 
 FULL = ["image_dit", "ring_share_r0", "ulysses_share", "full_sequence"]
