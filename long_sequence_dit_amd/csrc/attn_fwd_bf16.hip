@@ -10,7 +10,10 @@
 // fp32 (O, LSE) by log-sum-exp weights.
 //
 // Work decomposition: one workgroup = 8 waves = 256 query rows of one head,
-// one workgroup per CU (two waves per SIMD).
+// one workgroup per CU (two waves per SIMD).  When the query tiles leave the
+// last round of CUs part-full, that round's work is spread evenly instead
+// (the balanced tail): each of its workgroups takes an equal run of (query
+// tile, key tile) units and writes fp32 partials that a fix-up kernel merges.
 //  * each wave owns 32 query rows; its Q rows stay in VGPRs for the whole
 //    key loop as the B operand of v_mfma_f32_32x32x16_bf16;
 //  * scores are computed transposed, S^T = K Q^T, so every lane holds 32
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         __syncthreads();
 
         // Scores of alternate tiles (one buffer without kSpread: the softmax of tile t then reads
-        // it before the score MFMAs of tile t+1 overwrite it) and probabilities of alternate tiles.
+        // it before the score MFMAs of tile t+1 overwrite it).
         f32x16_t sA[2], sB_own[2];
         f32x16_t(&sB)[2] = kSpread ? sB_own : sA;
         u32x4_t pp[4];  // probabilities (one buffer suffices: see one_p_buffer_suffices)
