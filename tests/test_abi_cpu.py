@@ -218,3 +218,17 @@ def test_fp8_argument_errors(attn):
     # no-ops, even with NULL pointers
     assert f(q=None, k=None, v=None, o=None, lse=None, ws=None, Sq=0) == OK
     assert f(q=None, k=None, v=None, o=None, lse=None, ws=None, H=0) == OK
+
+
+def test_bench_tail_rule_matches_the_library(attn):
+    """bench.py reports which kernels a step launches with its own copy of the balanced tail's
+    rule; the FP8 workspace size (V^T tiles, plus the tail's slots exactly when the tail runs)
+    shows the library's decision, which must agree for every shape (256 CUs on the CPU build)."""
+    import bench
+    lib = attn.load()
+    for B, H, Sq, Skv in [(1, 16, 44160, 44160), (1, 4, 44160, 44160), (1, 16, 5520, 44160), (1, 24, 4608, 4608),
+                          (1, 16, 4096, 44160), (1, 3, 200, 5000), (1, 3, 200, 3000), (1, 2, 10, 20),
+                          (2, 7, 1000, 9000), (1, 1, 300, 8323072)]:
+        vt = B * H * -(-Skv // 64) * 8192
+        runs = lib.attn_fp8_workspace_size(B, H, Sq, Skv, 128) > vt
+        assert runs == bench.tail_runs(B * H * -(-Sq // 256), -(-Skv // 64), 256), (B, H, Sq, Skv)
