@@ -117,6 +117,14 @@ int64_t n_qtiles(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + lsdit
 size_t sk_o_bytes(int sk_wgs, int D) { return align_up((size_t)2 * sk_wgs * lsdit::kSkRows * D * 4); }
 size_t sk_bytes(int sk_wgs, int D) { return sk_o_bytes(sk_wgs, D) + align_up((size_t)2 * sk_wgs * lsdit::kSkRows * 4); }
 
+// The FP8 call's workspace: V^T tiles, then the balanced tail's partials when it runs.
+size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
+    return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
+}
+SkPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
+    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus());
+}
+
 int slots_for(uint32_t flags, int32_t n) {
     if (n <= 1) return 0;
     if (flags == ATTN_MERGE_NWAY) return n;
@@ -357,16 +365,6 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
                                   int32_t n, void* x, attn_strides_t xs, attn_stream_t stream) {
     return relayout(packed, x, xs, dt, B, H, S, D, n, false, (hipStream_t)stream);
 }
-
-namespace {
-// The FP8 call's workspace: V^T tiles, then the balanced tail's partials when it runs.
-size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
-    return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
-}
-SkPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
-    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus());
-}
-}  // namespace
 
 size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t Skv, int32_t D) {
     if (B <= 0 || H <= 0 || Sq < 0 || Skv <= 0 || D != 128) return 0;
