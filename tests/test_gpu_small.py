@@ -260,6 +260,25 @@ def test_strided_bshd_views():
     assert_parity(o, l, o_ref, l_ref, what="strided shard_fwd")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_balanced_tail_batches_and_strided_views(out_dtype):
+    """Two batches, [B,S,H,D] storage for Q, K, V and O, 5000 keys in two chunks: the 12 query
+    tiles run as 256 tail runs whose fix-up writes through the strided output."""
+    B, Sq, Skv, H, D = 2, 300, 5000, 3, 128
+    rng = np.random.default_rng(5)
+    qb, kb, vb = (synth.f32_to_bf16_bits(rng.standard_normal((B, S, H, D)).astype(np.float32))
+                  for S in (Sq, Skv, Skv))
+    qd, kd, vd = (to_device(x).permute(0, 2, 1, 3) for x in (qb, kb, vb))
+    qh, kh, vh = (np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (qb, kb, vb))
+    o_ref, l_ref = oracle.attention(qh, kh, vh, 1 / math.sqrt(D))
+    assert A().shard_workspace_size(B, H, Sq, D, 2, "fused") > 0
+    out = torch.empty((B, Sq, H, D), dtype=out_dtype, device="cuda").permute(0, 2, 1, 3)
+    o, l = A().shard_fwd(qd, kd, vd, (1700, 3300), (1, 0), mode="fused", out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    assert_parity(o, l, o_ref, l_ref, what="tail, B=2, strided, out %s" % out_dtype)
+
+
 def test_uniform_values_and_determinism():
     B, H, Sq, Skv, D = 1, 2, 256, 700, 128
     q, k, _ = _inputs(B, H, Sq, Skv, D, seed=8, qk=1.5)
