@@ -279,6 +279,27 @@ def test_balanced_tail_batches_and_strided_views(out_dtype):
     assert_parity(o, l, o_ref, l_ref, what="tail, B=2, strided, out %s" % out_dtype)
 
 
+def test_nonfinite_inputs_through_the_tail():
+    """One query tile against 79 key tiles runs as 79 one-tile runs merged by the fix-up: a NaN in
+    V still reaches every output of its column (and only that column), and a NaN in K, which
+    makes that key's score NaN in every row, every output and LSE."""
+    D = 128
+    q, k, v = _inputs(1, 1, 64, 5000, D, seed=10)
+    assert A().shard_workspace_size(1, 1, 64, D, 1, "fused") > 0
+    v[0, 0, 3000, 7] = 0x7FC0
+    o, l = A().shard_fwd(to_device(q), to_device(k), to_device(v), (5000,), None, mode="fused",
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[0, 0, :, 7]).all() and torch.isfinite(l).all()
+    assert torch.isfinite(o[0, 0, :, :7]).all() and torch.isfinite(o[0, 0, :, 8:]).all()
+    v[0, 0, 3000, 7] = v[0, 0, 3001, 7]
+    k[0, 0, 2000, 3] = 0x7FC0
+    o, l = A().shard_fwd(to_device(q), to_device(k), to_device(v), (5000,), None, mode="fused",
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all() and torch.isnan(l).all()
+
+
 def test_uniform_values_and_determinism():
     B, H, Sq, Skv, D = 1, 2, 256, 700, 128
     q, k, _ = _inputs(B, H, Sq, Skv, D, seed=8, qk=1.5)
