@@ -655,11 +655,10 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             }
         };
 
-        // ---- prologue.  Zero the tiles first: key rows past the end of a chunk are masked
-        // (P = 0), and zeros there keep 0 * V finite whatever the loads leave in those rows.
-        for (int i = (wave * 64 + lane_it); i < C::LDS_BYTES / 16; i += C::NT)
-            *(lds_u32x4_t*)(size_t)(lds_base + 16u * i) = u32x4_t{0u, 0u, 0u, 0u};
-        __syncthreads();
+        // ---- prologue.  LDS needs no clearing: every tile buffer is written whole by its loads
+        // before any read (all four K buffers and V_0, V_1 here, V_2 and V_3 by the first pair of
+        // iterations, before the P.V that reads them), rows past the tensor read as zeros and rows
+        // past a chunk are other rows of the tensor, which the mask gives P = 0.
 #pragma unroll
         for (int g = 0; g < C::NSTAGE; ++g) load_k(g);
 #pragma unroll

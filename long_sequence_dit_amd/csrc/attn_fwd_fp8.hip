@@ -507,9 +507,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         };
         auto valid_of = [&](int t) { return Skv - (g_first + t) * BK; };
 
-        // prologue: zero the buffers (rows past the end are masked; zeros keep 0 * V finite)
-        for (int i = tid; i < LDS_BYTES / 16; i += NT) *(lds_u32x4_t*)(size_t)(16u * i) = u32x4_t{0u, 0u, 0u, 0u};
-        __syncthreads();
+        // prologue (as in the bf16 kernel, LDS needs no clearing: every buffer is loaded whole
+        // before it is read; rows past the end read as zeros and are masked)
         // every K buffer, and the V tiles of the first pair of iterations (see below)
 #pragma unroll
         for (int g = 0; g < NSTAGE; ++g) load_k(g);
