@@ -30,8 +30,10 @@
  *    times the element size must be a multiple of 16 bytes.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the legacy default stream).  Nothing is synchronised by the library.
- *  - The caller owns every buffer.  The library allocates no device memory,
- *    keeps no state between calls, and is re-entrant.
+ *  - The caller owns every buffer.  The library allocates no device memory
+ *    and is re-entrant.  It keeps no state from one call to the next beyond
+ *    what it sets up once per device, thread-safely: that a kernel's LDS
+ *    size attribute is set.
  *  - Arguments are checked before anything is launched.  A non-OK status
  *    means nothing was enqueued and no output was touched, except
  *    ATTN_ERR_HIP, which reports a failed launch (a later kernel fault shows
@@ -66,10 +68,15 @@ typedef enum {
     ATTN_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned, or d stride not 1 */
     ATTN_ERR_UNSUPPORTED = 5, /* head dimension other than 64 or 128, too many chunks */
     ATTN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than attn_shard_workspace_size() */
-    ATTN_ERR_HIP = 7          /* a kernel launch failed */
+    ATTN_ERR_HIP = 7,         /* a kernel launch failed */
+    ATTN_STATUS_MAX_ENUM = 0x7FFFFFFF /* not a status: makes any int32 a valid value of the type */
 } attn_status_t;
 
-typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+typedef enum {
+    ATTN_F32 = 0,
+    ATTN_BF16 = 1,
+    ATTN_DTYPE_MAX_ENUM = 0x7FFFFFFF /* not a dtype: any int32 is a valid value (and rejected) */
+} attn_dtype_t;
 
 /* Element strides of the b, h and s indices; the d stride is always 1. */
 typedef struct {
@@ -84,7 +91,7 @@ typedef void* attn_stream_t;
 
 /* Merge modes of attn_shard_fwd (exactly one). */
 #define ATTN_MERGE_NWAY 1u   /* every chunk writes an fp32 partial; one n-way merge at the end */
-#define ATTN_MERGE_ONLINE 2u /* ring style: after each chunk, a pairwise merge into a running fp32 result */
+#define ATTN_MERGE_ONLINE 2u /* ring style: each chunk's kernel folds its result into a running fp32 result */
 #define ATTN_MERGE_FUSED 4u  /* one kernel walks all chunks in order, the online-softmax state in registers */
 
 /*
@@ -113,24 +120,31 @@ attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, at
  *
  *   o_parts, lse_parts   HOST arrays of n DEVICE pointers; part c is
  *                        [B, H, Sq, D] fp32 contiguous and [B, H, Sq] fp32.
- *   o_out                [B, H, Sq, D] o_dt, strides os
+ *   o_out                [B, H, Sq, D] o_dt, strides os (element strides,
+ *                        so the merged output can go straight into a view
+ *                        such as [B, S, H, D] storage)
  *   lse_out              [B, H, Sq] fp32 contiguous
  * 1 <= n <= ATTN_MAX_CHUNKS.  With o_dt = ATTN_F32 and contiguous strides,
  * o_out may alias o_parts[0] and lse_out may alias lse_parts[0] (the ring's
- * in-place online merge); no other overlap is allowed.
+ * in-place online merge); no other overlap is allowed.  Parts with LSE -inf
+ * carry no weight; a NaN LSE in any part makes the row's O and LSE NaN (as
+ * attention over all the keys in one pass gives for a NaN query row).
  */
 attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
                              int32_t H, int32_t Sq, int32_t D, void* o_out, attn_strides_t os, attn_dtype_t o_dt,
                              float* lse_out, attn_stream_t stream);
 
 /*
- * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd needs
- * for this shape, chunk count and merge mode: n fp32 partials (O and LSE) for
- * ATTN_MERGE_NWAY, two for ATTN_MERGE_ONLINE.  For ATTN_MERGE_FUSED (and any
- * mode when n_chunks == 1) no chunk partials are needed; the size returned is
- * the room for the balanced tail (see attn_shard_fwd) of a shape whose query
- * tiles of 256 rows leave the last round of the current device's CUs
- * part-full: 2 * CUs * 256 * (D + 1) fp32 values (0 when they fill whole rounds).
+ * attn_shard_workspace_size — bytes of device workspace attn_shard_fwd uses
+ * for this shape, chunk count and merge mode: first the chunk slots, fp32
+ * results [B,H,Sq,D] plus their LSE [B,H,Sq] (each part 256-byte aligned):
+ * n of them for ATTN_MERGE_NWAY, one (the running result) for
+ * ATTN_MERGE_ONLINE, none for ATTN_MERGE_FUSED or when n_chunks == 1.  Then,
+ * for a shape whose query tiles of 256 rows leave the last round of the
+ * current device's CUs part-full, room for the balanced tail (see
+ * attn_shard_fwd): 2 * CUs * 256 * (D + 1) fp32 values (nothing when the
+ * tiles fill whole rounds).  The slots are required; the tail's room is
+ * optional (without it, whole query tiles throughout).
  * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
  */
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
@@ -157,11 +171,15 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *              merges the runs' fp32 partials by their LSE (the balanced tail;
  *              only with the workspace: none given, whole tiles throughout).
  *              ONLINE and NWAY run one kernel per chunk
- *              and merge the fp32 partials with attn_lse_merge's kernel, after
- *              every chunk (as a ring receiving one block per step does) or
- *              once at the end.
- *   workspace  DEVICE buffer of ws_bytes >= attn_shard_workspace_size(...),
- *              16-byte aligned (may be NULL when that size is 0)
+ *              (each with the balanced tail when it pays).  ONLINE is the
+ *              ring's step: each chunk's kernel folds its result into the
+ *              running fp32 result by the LSE rule in its epilogue (the last
+ *              one into o and lse).  NWAY writes each chunk's fp32 partial and
+ *              merges them all at the end with attn_lse_merge's kernel.
+ *   workspace  DEVICE buffer, 16-byte aligned, of attn_shard_workspace_size()
+ *              bytes; at least its chunk slots are required
+ *              (ATTN_ERR_WORKSPACE otherwise), the tail's room after them is
+ *              used when present (may be NULL when no slots are needed)
  *   o, lse     as in attn_chunk_fwd, for the whole key sequence
  * 1 <= n_chunks <= ATTN_MAX_CHUNKS.  The result equals attention over all
  * Skv keys up to rounding, whatever the chunking and order.

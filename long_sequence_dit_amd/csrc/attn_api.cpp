@@ -14,7 +14,9 @@
 #include "attn.h"
 
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
+
 
 #include "kernels.h"
 
@@ -81,6 +83,17 @@ size_t slot_bytes(int32_t B, int32_t H, int32_t Sq, int32_t D) {
     return align_up(rows * D * 4) + align_up(rows * 4);
 }
 
+// Debug aid: LSDIT_DEBUG_WG_ORDER=reverse (or rotate) dispatches the forward kernels' logical
+// workgroups in reversed (or half-rotated) order, so that a test can check that results do not
+// depend on which workgroups run together or first.
+int debug_wg_order() {
+    const char* e = getenv("LSDIT_DEBUG_WG_ORDER");
+    if (!e) return 0;
+    if (strcmp(e, "reverse") == 0) return 1;
+    if (strcmp(e, "rotate") == 0) return 2;
+    return 0;
+}
+
 int device_cus() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -91,22 +104,24 @@ int device_cus() {
 // The balanced tail of the bf16 kernel (FwdArgs): when its n_q query tiles leave CUs idle in
 // the last round, the full rounds run whole query tiles and the last round's work is spread
 // evenly over the CUs as runs of (query tile, key tile) units, whose partials the fix-up kernel
-// merges.  Worth it when the idle part of the last round is at least kSkMinSaving key tiles
-// per CU: the runs' pipeline fill and drain, their partials and the fix-up launch cost about
-// as much as 20-30 key tiles (at 22 tiles, the 4,608-token image shape ran 4.5% slower with the
-// tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).
+// merges.  Worth it when the idle part of the last round is at least min_saving key tiles per
+// CU: the runs' pipeline fill and drain, their partials and the fix-up launch cost about as much
+// as 20-30 key tiles (bf16: at 22 tiles, the 4,608-token image shape ran 4.5% slower with the
+// tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).  The FP8
+// kernel's tiles take half the time, so its fixed costs weigh about twice as many tiles.
 struct SkPlan {
     int n_dp = 0;    // query tiles run whole
     int sk_wgs = 0;  // workgroups of the tail (0 = no tail)
 };
-constexpr int64_t kSkMinSaving = 64;
+constexpr int64_t kSkMinSavingBf16 = 40;
+constexpr int64_t kSkMinSavingFp8 = 64;
 
-SkPlan sk_plan(int64_t n_q, int64_t T, int cus) {
+SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving) {
     SkPlan p;
     if (n_q <= 0 || T <= 0 || cus <= 0 || n_q > 0x7FFFFFFF) return p;
     const int64_t rem = n_q % cus;
-    if (rem == 0 || T * (cus - rem) / cus < kSkMinSaving) return p;
-    const int64_t U = rem * T;  // > rem, since T >= kSkMinSaving: every run is at most T long
+    if (rem == 0 || T * (cus - rem) / cus < min_saving) return p;
+    const int64_t U = rem * T;  // > rem, since T > min_saving >= 1: every run is at most T long
     p.n_dp = (int)(n_q - rem);
     p.sk_wgs = (int)(U < cus ? U : cus);
     return p;
@@ -122,89 +137,29 @@ size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
     return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
 }
 SkPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
-    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus());
+    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus(), kSkMinSavingFp8);
 }
 
+// fp32 chunk slots of a schedule: NWAY keeps every chunk's partial, ONLINE one running result
+// (each chunk's launch folds into it in its epilogue), FUSED none (one kernel, no partials).
 int slots_for(uint32_t flags, int32_t n) {
     if (n <= 1) return 0;
     if (flags == ATTN_MERGE_NWAY) return n;
-    if (flags == ATTN_MERGE_ONLINE) return 2;
-    if (flags == ATTN_MERGE_FUSED) return 0;  // one kernel, no partials
+    if (flags == ATTN_MERGE_ONLINE) return 1;
+    if (flags == ATTN_MERGE_FUSED) return 0;
     return -1;
 }
 
+
 }  // namespace
 
-extern "C" {
+namespace {
 
-attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
-                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t Skv,
-                             int32_t D, float scale, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
-                             attn_stream_t stream) {
-    if (Skv < 0) return ATTN_ERR_SHAPE;
-    bool noop = false;
-    attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, Skv, D, scale, o, os, o_dt, lse, &noop);
-    if (st != ATTN_OK || noop) return st;
-    const hipStream_t s = (hipStream_t)stream;
-    if (Skv == 0)  // no keys: O = 0, LSE = -inf
-        return lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s) == hipSuccess
-                   ? ATTN_OK
-                   : ATTN_ERR_HIP;
-    FwdArgs a{};
-    a.q = q; a.k = k; a.v = v;
-    a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
-    a.o = o; a.os = S(os); a.o_bf16 = o_dt == ATTN_BF16;
-    a.lse = lse;
-    a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
-    a.scale = scale;
-    a.n_chunks = 1;
-    a.chunk_row[0] = 0;
-    a.chunk_len[0] = Skv;
-    return run_fwd(a, in_dt, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
-                             int32_t H, int32_t Sq, int32_t D, void* o_out, attn_strides_t os, attn_dtype_t o_dt,
-                             float* lse_out, attn_stream_t stream) {
-    if (!valid_dtype(o_dt)) return ATTN_ERR_DTYPE;
-    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-    if (n < 1 || B < 0 || H < 0 || Sq < 0) return ATTN_ERR_SHAPE;
-    if (n > ATTN_MAX_CHUNKS || n > lsdit::kMaxMergeParts) return ATTN_ERR_UNSUPPORTED;
-    if ((int64_t)B * H * Sq == 0) return ATTN_OK;
-    if (!o_parts || !lse_parts || !o_out || !lse_out) return ATTN_ERR_NULL;
-    MergeArgs m{};
-    for (int c = 0; c < n; ++c) {
-        if (!o_parts[c] || !lse_parts[c]) return ATTN_ERR_NULL;
-        if (!aligned16(o_parts[c]) || !aligned16(lse_parts[c])) return ATTN_ERR_ALIGN;
-        m.o_parts[c] = o_parts[c];
-        m.lse_parts[c] = lse_parts[c];
-    }
-    if (!aligned16(o_out) || !aligned16(lse_out) || !strides_ok(os, esize(o_dt))) return ATTN_ERR_ALIGN;
-    m.n = n;
-    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
-    m.o = o_out; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse_out;
-    return lsdit::launch_lse_merge(m, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
-
-size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags) {
-    if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
-    if (flags == ATTN_MERGE_FUSED || n_chunks == 1) {
-        // room for the balanced tail of shapes whose query tiles leave the last round part-full
-        // (whether it runs also depends on the key count)
-        const int cus = device_cus();
-        const int64_t n_q = n_qtiles(B, H, Sq);
-        return n_q % cus != 0 ? sk_bytes(cus, D) : 0;
-    }
-    const int slots = slots_for(flags, n_chunks);
-    if (slots <= 0) return 0;
-    return (size_t)slots * slot_bytes(B, H, Sq, D);
-}
-
-attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+// The shard driver behind attn_shard_fwd.
+attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
                              attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t D,
                              float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
-                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
-                             attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
+                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
     // ---- chunk plan (host): lengths, offsets, processing order
     if (n_chunks < 1) return ATTN_ERR_SHAPE;
     if (n_chunks > ATTN_MAX_CHUNKS) return ATTN_ERR_UNSUPPORTED;
@@ -239,10 +194,19 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     for (int t = 0; t < n_chunks; ++t)
         if (chunk_len[ord[t]] > 0) live[n_live++] = ord[t];
 
-    const size_t need = slots_for(flags, n_chunks) > 0 ? attn_shard_workspace_size(B, H, Sq, D, n_chunks, flags) : 0;
-    if (n_live > 1 && need > 0) {
-        if (!workspace || ws_bytes < need) return ATTN_ERR_WORKSPACE;
-        if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return ATTN_ERR_ALIGN;
+    // workspace: the chunk slots of the per-chunk schedules, then the balanced tail's partials
+    const int n_slots = slots_for(flags, n_chunks) > 0 ? slots_for(flags, n_chunks) : 0;
+    const size_t slots_need = (size_t)n_slots * slot_bytes(B, H, Sq, D);
+    const bool ws_aligned = (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0;
+    if (n_live > 1 && n_slots > 0) {
+        if (!workspace || ws_bytes < slots_need) return ATTN_ERR_WORKSPACE;
+        if (!ws_aligned) return ATTN_ERR_ALIGN;
+    }
+    void* tail_ws = nullptr;
+    size_t tail_bytes = 0;
+    if (workspace && ws_aligned && ws_bytes > slots_need) {
+        tail_ws = (char*)workspace + slots_need;
+        tail_bytes = ws_bytes - slots_need;
     }
 
     const hipStream_t s = (hipStream_t)stream;
@@ -250,6 +214,7 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     base.q = q; base.k = k; base.v = v;
     base.qs = S(qs); base.ks = S(ks); base.vs = S(vs);
     base.B = B; base.H = H; base.Sq = Sq; base.Skv = (int32_t)total; base.D = D; base.scale = scale;
+    base.wg_order = debug_wg_order();
     auto chunk_args = [&](int c) {  // one chunk, by its rows in the k and v tensors
         FwdArgs a = base;
         a.n_chunks = 1;
@@ -264,7 +229,38 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
     const Strides cs = contiguous(H, Sq, D);
     auto slot_o = [&](int i) { return (float*)((char*)workspace + (size_t)i * slot_bytes(B, H, Sq, D)); };
     auto slot_lse = [&](int i) { return (float*)((char*)slot_o(i) + align_up(rows * D * 4)); };
+    auto to_slot = [&](FwdArgs& a, int i) {
+        a.o = slot_o(i); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(i);
+    };
     auto ok = [](hipError_t e) { return e == hipSuccess; };
+    const int64_t n_q = n_qtiles(B, H, Sq);
+    const int cus = device_cus();
+
+    // One kernel launch over a's chunk list (T key tiles) into a's output, folding in a's running
+    // result if it has one.  When its query tiles leave the last round of CUs part-full, that
+    // round's work is spread evenly (the balanced tail) as far as the tail's room allows, and the
+    // fix-up kernel merges the runs' partials (and the running result) into the output.
+    auto launch = [&](FwdArgs a, int64_t T) -> attn_status_t {
+        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, cus, kSkMinSavingBf16) : SkPlan{};
+        void* tw = tail_ws;
+        const size_t tb = tail_bytes;
+        if (p.sk_wgs == 0 || !tw || tb < sk_bytes(p.sk_wgs, D)) return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        a.n_dp = p.n_dp;
+        a.sk_wgs = p.sk_wgs;
+        a.sk_o = (float*)tw;
+        a.sk_lse = (float*)((char*)tw + sk_o_bytes(p.sk_wgs, D));
+        if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
+        lsdit::SkFixupArgs f{};
+        f.B = B; f.H = H; f.Sq = Sq; f.D = D;
+        f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
+        f.T = (int)T;
+        f.n_dp = p.n_dp; f.n_q = (int)n_q; f.sk_wgs = p.sk_wgs;
+        f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
+        f.o = a.o; f.os = a.os; f.o_bf16 = a.o_bf16; f.lse = a.lse;
+        f.run_o = a.run_o; f.run_lse = a.run_lse;
+        return ok(lsdit::launch_sk_fixup(f, s)) ? ATTN_OK : ATTN_ERR_HIP;
+    };
+    auto tiles = [](int64_t len) { return (len + 63) / 64; };  // key tiles, as the kernel counts them
 
     if (n_live == 0) {
         return ok(lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s)) ? ATTN_OK
@@ -274,68 +270,122 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
         // one kernel walks the chunks in processing order, the online-softmax state in registers
         FwdArgs a = base;
         a.n_chunks = n_live;
+        int64_t T = 0;
         for (int t = 0; t < n_live; ++t) {
             a.chunk_row[t] = (int32_t)off[live[t]];
             a.chunk_len[t] = chunk_len[live[t]];
+            T += tiles(chunk_len[live[t]]);
         }
         to_final(a);
-        // query tiles that leave the last round part-full: spread that round's work evenly
-        // (the balanced tail), as far as the workspace allows
-        const bool ws_ok = workspace && (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0;
-        int64_t T = 0;  // key tiles of the chunk list, as the kernel counts them
-        for (int t = 0; t < n_live; ++t) T += (chunk_len[live[t]] + 63) / 64;
-        const int64_t n_q = n_qtiles(B, H, Sq);
-        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, device_cus()) : SkPlan{};
-        if (p.sk_wgs == 0 || !ws_ok || ws_bytes < sk_bytes(p.sk_wgs, D))
-            return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
-        a.n_dp = p.n_dp;
-        a.sk_wgs = p.sk_wgs;
-        a.sk_o = (float*)workspace;
-        a.sk_lse = (float*)((char*)workspace + sk_o_bytes(p.sk_wgs, D));
-        if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
-        lsdit::SkFixupArgs f{};
-        f.B = B; f.H = H; f.Sq = Sq; f.D = D;
-        f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
-        f.T = (int)T;
-        f.n_dp = p.n_dp; f.n_q = (int)n_q; f.sk_wgs = p.sk_wgs;
-        f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
-        f.o = o; f.os = S(os); f.o_bf16 = o_dt == ATTN_BF16; f.lse = lse;
-        return ok(lsdit::launch_sk_fixup(f, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        return launch(a, T);
     }
 
-    MergeArgs m{};
-    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
     if (flags == ATTN_MERGE_ONLINE) {
+        // as a ring receiving one chunk per step: each chunk's launch folds its result into the
+        // running fp32 result in slot 0 (in place; the last one into the final output) in its
+        // epilogue, by the LSE rule
         for (int t = 0; t < n_live; ++t) {
             FwdArgs a = chunk_args(live[t]);
-            const int slot = t == 0 ? 0 : 1;
-            a.o = slot_o(slot); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(slot);
-            if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
-            if (t == 0) continue;
-            m.n = 2;
-            m.o_parts[0] = slot_o(0); m.lse_parts[0] = slot_lse(0);
-            m.o_parts[1] = slot_o(1); m.lse_parts[1] = slot_lse(1);
-            if (t == n_live - 1) {
-                m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
-            } else {
-                m.o = slot_o(0); m.os = cs; m.o_bf16 = 0; m.lse = slot_lse(0);
+            if (t > 0) {
+                a.run_o = slot_o(0);
+                a.run_lse = slot_lse(0);
             }
-            if (!ok(lsdit::launch_lse_merge(m, s))) return ATTN_ERR_HIP;
+            if (t == n_live - 1) to_final(a);
+            else to_slot(a, 0);
+            const attn_status_t st = launch(a, tiles(chunk_len[live[t]]));
+            if (st != ATTN_OK) return st;
         }
         return ATTN_OK;
     }
 
-    // ATTN_MERGE_NWAY
+    // ATTN_MERGE_NWAY: every chunk's fp32 partial in its own slot, then one n-way merge
+    MergeArgs m{};
+    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
     for (int t = 0; t < n_live; ++t) {
         FwdArgs a = chunk_args(live[t]);
-        a.o = slot_o(t); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(t);
-        if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
+        to_slot(a, t);
+        const attn_status_t st = launch(a, tiles(chunk_len[live[t]]));
+        if (st != ATTN_OK) return st;
         m.o_parts[t] = slot_o(t);
         m.lse_parts[t] = slot_lse(t);
     }
     m.n = n_live;
     m.o = o; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse;
     return ok(lsdit::launch_lse_merge(m, s)) ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_chunk_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t Skv,
+                             int32_t D, float scale, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                             attn_stream_t stream) {
+    if (Skv < 0) return ATTN_ERR_SHAPE;
+    bool noop = false;
+    attn_status_t st = check_common(q, qs, k, ks, v, vs, in_dt, B, H, Sq, Skv, D, scale, o, os, o_dt, lse, &noop);
+    if (st != ATTN_OK || noop) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    if (Skv == 0)  // no keys: O = 0, LSE = -inf
+        return lsdit::launch_fill_empty(o, S(os), o_dt == ATTN_BF16, lse, B, H, Sq, D, s) == hipSuccess
+                   ? ATTN_OK
+                   : ATTN_ERR_HIP;
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v;
+    a.qs = S(qs); a.ks = S(ks); a.vs = S(vs);
+    a.o = o; a.os = S(os); a.o_bf16 = o_dt == ATTN_BF16;
+    a.lse = lse;
+    a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv; a.D = D;
+    a.scale = scale;
+    a.n_chunks = 1;
+    a.chunk_row[0] = 0;
+    a.chunk_len[0] = Skv;
+    a.wg_order = debug_wg_order();
+    return run_fwd(a, in_dt, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float* const* lse_parts, int32_t B,
+                             int32_t H, int32_t Sq, int32_t D, void* o_out, attn_strides_t os, attn_dtype_t o_dt,
+                             float* lse_out, attn_stream_t stream) {
+    if (!valid_dtype(o_dt)) return ATTN_ERR_DTYPE;
+    if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+    if (n < 1 || B < 0 || H < 0 || Sq < 0) return ATTN_ERR_SHAPE;
+    if (n > ATTN_MAX_CHUNKS || n > lsdit::kMaxMergeParts) return ATTN_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * Sq == 0) return ATTN_OK;
+    if (!o_parts || !lse_parts || !o_out || !lse_out) return ATTN_ERR_NULL;
+    MergeArgs m{};
+    for (int c = 0; c < n; ++c) {
+        if (!o_parts[c] || !lse_parts[c]) return ATTN_ERR_NULL;
+        if (!aligned16(o_parts[c]) || !aligned16(lse_parts[c])) return ATTN_ERR_ALIGN;
+        m.o_parts[c] = o_parts[c];
+        m.lse_parts[c] = lse_parts[c];
+    }
+    if (!aligned16(o_out) || !aligned16(lse_out) || !strides_ok(os, esize(o_dt))) return ATTN_ERR_ALIGN;
+    m.n = n;
+    m.B = B; m.H = H; m.Sq = Sq; m.D = D;
+    m.o = o_out; m.os = S(os); m.o_bf16 = o_dt == ATTN_BF16; m.lse = lse_out;
+    return lsdit::launch_lse_merge(m, (hipStream_t)stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags) {
+    if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
+    const int slots = slots_for(flags, n_chunks);
+    if (slots < 0) return 0;
+    // the chunk slots, then room for the balanced tail of shapes whose query tiles leave the last
+    // round part-full (whether it runs also depends on the key count)
+    const int cus = device_cus();
+    const int64_t n_q = n_qtiles(B, H, Sq);
+    return (size_t)slots * slot_bytes(B, H, Sq, D) + (n_q % cus != 0 ? sk_bytes(cus, D) : 0);
+}
+
+attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
+                             attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t D,
+                             float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
+                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
+                             attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
+    return shard_fwd_impl(q, qs, k, ks, v, vs, in_dt, B, H, Sq, D, scale, n_chunks, chunk_len, order, flags,
+                          workspace, ws_bytes, o, os, o_dt, lse, stream);
 }
 
 namespace {
@@ -407,6 +457,7 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     a.B = B; a.H = H; a.Sq = Sq; a.Skv = Skv;
     a.c = (float)((double)scale * 1.4426950408889634 * (double)q_descale * (double)k_descale);
     a.v_descale = v_descale;
+    a.wg_order = debug_wg_order();
     if (!(a.c > 0.f) || !isfinite(a.c)) return ATTN_ERR_SHAPE;
     // the balanced tail, as in attn_shard_fwd, its partials after V^T in the workspace
     const SkPlan p = fp8_plan(B, H, Sq, Skv);
@@ -439,6 +490,7 @@ const char* attn_status_str(attn_status_t s) {
         case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, chunk count or merge mode";
         case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
+        default: break;
     }
     return "unknown status";
 }

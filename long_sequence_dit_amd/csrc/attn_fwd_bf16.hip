@@ -6,8 +6,7 @@
 // in key/value blocks one at a time without materialising the full K and V
 // (NVIDIA Technical Blog "Scaling AI Inference Across Multiple GPUs Using
 // NVIDIA TensorRT with Multi-Device Inference Support", section "Ring
-// Attention").  Optionally the epilogue merges the result into a running
-// fp32 (O, LSE) by log-sum-exp weights.
+// Attention").
 //
 // Work decomposition: one workgroup = 8 waves = 256 query rows of one head,
 // one workgroup per CU (two waves per SIMD).  When the query tiles leave the
@@ -46,12 +45,14 @@
 //    and the transposed reads of V are free of bank conflicts;
 //  * exponentials are base 2 with scale*log2(e) folded into one FMA; the
 //    running output is rescaled only when a row maximum grows by more than
-//    2^8.
+//    8 (log2 units) past the one it was last rescaled to, and the weights,
+//    taken against that maximum plus 8, stay at most 1.
 // Workgroups are remapped so that each XCD (workgroups are dealt to the 8
 // XCDs round-robin) runs consecutive query tiles of the same head, which
 // then share K/V tiles in that XCD's L2.
 #include "kernels.h"
 
+#include <atomic>
 #include <math.h>
 #include <stddef.h>
 
@@ -134,6 +135,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// A weight 2^x, x <= 0 (so at most 1).  The clamp to [0, 1] folds into the exponential
+// (v_exp_f32 ... clamp) and maps NaN to 0: a NaN query row (every score NaN) then adds nothing
+// to the row-sum MFMA, whose zero entries would otherwise carry the NaN into the sum of the
+// query sharing its MFMA column.  The NaN still reaches the row's own output, through its
+// reference and scale factor (see the lazy rescale).
+__device__ __forceinline__ float weight_exp2(float x) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.f, 1.f);
+}
 
 // {x of lane l%32, x of lane l%32 + 32} on every lane.
 __device__ __forceinline__ void half_pair(float x, float& a, float& b) {
@@ -177,8 +186,8 @@ __device__ __forceinline__ float from_lane(int src, float x) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(x)));
 }
 
-// Buffer resource of a K or V head: base, no stride, num_records bytes; reads past the
-// end return zeros.
+// Buffer resource: base, no stride, num_records bytes; reads at or past num_records return
+// zeros.
 struct Rsrc {
     i32x4_t w;
 };
@@ -191,6 +200,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
     r.w[3] = 0x00020000;
     return r;
 }
+// Resource of one tile: the bytes [off, end) of a head's rows, rebased to off (empty when off >=
+// end).  The raw-buffer range check applies to the per-lane offset, not to a scalar offset, so
+// every tile gets a resource of its own: the rows of a last partial tile past the tensor's end,
+// and the tiles prefetched past the last chunk, then read as zeros instead of whatever memory
+// follows the tensor.  Wave-uniform, so all of it is scalar arithmetic.
+__device__ __forceinline__ Rsrc tile_rsrc(const void* base, int off, int end) {
+    return make_rsrc((const unsigned char*)base + off, off < end ? end - off : 0);
+}
 
 // NB wave-wide 16-byte-per-lane loads into consecutive 1 KiB LDS blocks at LDS byte address
 // dst.  Written as assembly on purpose: for the builtin form the compiler assumes that any
@@ -202,14 +219,14 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
 // address (an operand of the statement, so the compiler sets it and knows it is used);
 // one wait state separates its write from the load.
 template <int NB>
-__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB], int soff) {
+__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
         asm volatile(
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %0, %1, %2 offen lds"
+            "buffer_load_dwordx4 %0, %1, 0 offen lds"
             :
-            : "v"(goff[i]), "s"(rs.w), "s"(soff), "{m0}"(dst + i * 1024u)
+            : "v"(goff[i]), "s"(rs.w), "{m0}"(dst + i * 1024u)
             : "memory");
 }
 
@@ -260,7 +277,7 @@ template <int D>
 struct Wave {
     f32x16_t acc[D / 32];  // O^T accumulators
     bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
-    float m_run;           // reference max (scaled, log2 domain)
+    float m_run;           // softmax reference (scaled, log2 domain): a row max + kRescale
     f32x4_t lacc;          // row sums (every element; lanes 16-47 hold their partner's query)
     bf16x8_t rs_a;         // A operand of the row-sum MFMA
     unsigned k_lane[D / 16];  // per-lane LDS read address of K operand kk in K buffer 0
@@ -324,8 +341,8 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
             sm.x[J][1] = __builtin_fmaf(x1, c, -sm.m_new);
             pin(sm.x[J][0], sm.x[J][1]);
         } else if constexpr (POS == a + 1) {
-            sm.e[J][0] = fast_exp2(sm.x[J][0]);
-            sm.e[J][1] = fast_exp2(sm.x[J][1]);
+            sm.e[J][0] = weight_exp2(sm.x[J][0]);
+            sm.e[J][1] = weight_exp2(sm.x[J][1]);
             pin(sm.e[J][0], sm.e[J][1]);
         } else if constexpr (POS == a + 2) {
             unsigned word = pack_bf16(sm.e[J][0], sm.e[J][1]);
@@ -356,12 +373,14 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
                               vmax(sm.mt[9], sm.mt[10]));
         half_pair(mx, sm.m0, sm.m1);
     } else if constexpr (POS == 4) {
-        // Lazy rescale: a row's reference max only moves when the row's max exceeds it by
-        // more than kRescale (log2 units).  Weights are then at most 2^kRescale, harmless in
-        // fp32 and bf16, and O and l stay consistent because both use the same reference.
-        // Lanes l and l+32 hold the same row and take the same decision.
+        // Lazy rescale.  A row's reference r sits kRescale (log2 units) above the row max it
+        // was last moved to, and moves only when a tile's row max m exceeds it, or is NaN: to
+        // m + kRescale.  So every weight 2^(s c - r) is at most 1 (at most 2^-kRescale right
+        // after a move), O and l share the reference (consistent), and LSE = r + log2 l.  A NaN
+        // row max (a NaN score) moves the reference to NaN, which makes the rescale factor and
+        // so the row's output and LSE NaN.  Lanes l and l+32 hold the same row and agree.
         const float m_tile = vmax(sm.m0, sm.m1) * w.c;  // max(m0, m1)
-        sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
+        sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
     }
@@ -504,18 +523,19 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         const kernarg_t<FwdArgs>* ap = (const kernarg_t<FwdArgs>*)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
         const kernarg_t<FwdArgs>& ar = *ap;
+        const int bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
         // likewise the lane index: values derived from it are computed in the iteration
         int lane_it = lane;
         asm volatile("" : "+v"(lane_it));
         const int hi_it = lane_it >> 5;
         int sk_w = -1, tile, g_first, nkt;
-        if (ar.sk_wgs == 0 || (int)blockIdx.x < ar.n_dp) {
+        if (ar.sk_wgs == 0 || bid < ar.n_dp) {
             if (seg > 0) break;
-            tile = xcd_remap(blockIdx.x, ar.sk_wgs == 0 ? n_qtiles : ar.n_dp);
+            tile = xcd_remap(bid, ar.sk_wgs == 0 ? n_qtiles : ar.n_dp);
             g_first = 0;
             nkt = nkt_all;
         } else {
-            sk_w = xcd_remap(blockIdx.x - ar.n_dp, ar.sk_wgs);
+            sk_w = xcd_remap(bid - ar.n_dp, ar.sk_wgs);
             const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1
@@ -564,11 +584,10 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 
         // ---- K/V loads straight into LDS.  One wave-wide instruction fills a contiguous
         // 1 KiB block (lane_it L -> bytes 16L..16L+15); lane_it L fetches the global chunk that the
-        // swizzle maps to its slot.  Offsets are per lane_it and fixed; tiles advance by a scalar.
-        // Loads of tiles past the chunk fall outside the buffer and read zeros.
+        // swizzle maps to its slot.  Offsets are per lane_it and fixed; each tile gets a resource
+        // based at its first row (tile_rsrc), so rows past the tensor read zeros.
         const int k_rs = (int)(ar.ks.s * 2), v_rs = (int)(ar.vs.s * 2);  // row pitch in bytes
-        const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D * 2);
-        const Rsrc vrs = make_rsrc(vp, (Skv - 1) * v_rs + D * 2);
+        const int k_end = (Skv - 1) * k_rs + D * 2, v_end = (Skv - 1) * v_rs + D * 2;  // bytes of a head's rows
         int k_goff[C::BLKS_PER_WAVE], v_goff[C::BLKS_PER_WAVE];
 #pragma unroll
         for (int i = 0; i < C::BLKS_PER_WAVE; ++i) {
@@ -596,13 +615,14 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         wm = wk;
         auto load_k = [&](int g) {
             if (wave < C::LOADERS)
-                lds_dma<C::BLKS_PER_WAVE>(krs, lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff, wk.row * k_rs);
+                lds_dma<C::BLKS_PER_WAVE>(tile_rsrc(kp, wk.row * k_rs, k_end),
+                                          lds_base + kbuf(g) + wave * C::BLKS_PER_WAVE * 1024, k_goff);
             wk.next(n_chunks, v_row, v_len, Skv);
         };
         auto load_v = [&](int g) {
             if (wave < C::LOADERS)
-                lds_dma<C::BLKS_PER_WAVE>(vrs, lds_base + C::V_REGION + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff,
-                                          wv.row * v_rs);
+                lds_dma<C::BLKS_PER_WAVE>(tile_rsrc(vp, wv.row * v_rs, v_end),
+                                          lds_base + C::V_REGION + vbuf(g) + wave * C::BLKS_PER_WAVE * 1024, v_goff);
             wv.next(n_chunks, v_row, v_len, Skv);
         };
         auto next_valid = [&]() {  // valid keys of the next tile to mask
@@ -740,12 +760,30 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // P.V of the last tile
         stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pp, sA, sA, pp, sm);
 
-        // ---- epilogue: normalise, LSE, store (the final output; or, for a stream-K segment, an
-        // fp32 partial and its LSE in the segment's slot)
+        // ---- epilogue: normalise, LSE, fold in the running result if there is one, store (the
+        // final output; or, for a stream-K segment, an fp32 partial and its LSE in the segment's
+        // slot)
         const float l_tot = from_lane(rowsum_partner(lane_it), w.lacc[0]);
         const float inv_l = 1.f / l_tot;
         const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
         if (qrow < ar.Sq) {
+            // output element o = wc * acc + wr * O_run (wc = 1/l without a running result)
+            float lse_out = lse2 * kLn2, wc = inv_l, wr = 0.f;
+            const float* rp = nullptr;
+            if (sk_w < 0 && ar.run_lse) {
+                const int64_t rrow = (int64_t)bh * ar.Sq + qrow;
+                rp = ar.run_o + rrow * D + 4 * hi_it;
+                lse_out = fold_weights(lse_out, ar.run_lse[rrow], wc, wr);
+                wc *= inv_l;
+            }
+            // the 4 output values of accumulator group (dt, r4): d = 32 dt + 8 r4 + 4 hi .. +3
+            auto vals = [&](int dt, int r4) __attribute__((always_inline)) {
+                f32x4_t x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * wc;
+                if (rp) x += wr * *(const f32x4_t*)(rp + 32 * dt + 8 * r4);
+                return x;
+            };
             if (sk_w < 0 && ar.o_bf16) {
                 unsigned short* op = (unsigned short*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
 #pragma unroll
@@ -753,12 +791,13 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
                         const int d = 32 * dt + 8 * r4 + 4 * hi_it;
+                        const f32x4_t x = vals(dt, r4);
                         u32x2_t wd;
-                        wd[0] = pack_bf16(w.acc[dt][4 * r4] * inv_l, w.acc[dt][4 * r4 + 1] * inv_l);
-                        wd[1] = pack_bf16(w.acc[dt][4 * r4 + 2] * inv_l, w.acc[dt][4 * r4 + 3] * inv_l);
+                        wd[0] = pack_bf16(x[0], x[1]);
+                        wd[1] = pack_bf16(x[2], x[3]);
                         *(u32x2_t*)(op + d) = wd;
                     }
-                if (hi_it == 0) ar.lse[(int64_t)bh * ar.Sq + qrow] = lse2 * kLn2;
+                if (hi_it == 0) ar.lse[(int64_t)bh * ar.Sq + qrow] = lse_out;
             } else {
                 float* op;
                 float* lp;
@@ -773,14 +812,8 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) {
-                        const int d = 32 * dt + 8 * r4 + 4 * hi_it;
-                        f32x4_t x;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x[e] = w.acc[dt][4 * r4 + e] * inv_l;
-                        *(f32x4_t*)(op + d) = x;
-                    }
-                if (hi_it == 0) *lp = lse2 * kLn2;
+                    for (int r4 = 0; r4 < 4; ++r4) *(f32x4_t*)(op + 32 * dt + 8 * r4 + 4 * hi_it) = vals(dt, r4);
+                if (hi_it == 0) *lp = lse_out;
             }
         }
     }
@@ -789,15 +822,17 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     using C = Cfg<D>;
-    static bool attr_set[64] = {};
+    // per device: the kernel's dynamic LDS limit has been raised (an atomic flag, so that
+    // first calls from several threads are safe: each may set the attribute, which is idempotent)
+    static std::atomic<bool> attr_set[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
         e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 C::LDS_BYTES);
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+        if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
     }
     const int n_qt = (a.Sq + C::BQ - 1) / C::BQ;
     const int64_t n_q = (int64_t)a.B * a.H * n_qt;

@@ -99,11 +99,20 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdArgs a, int n_qt, 
     }
 
     if (qrow >= a.Sq) return;
-    const float inv_l = 1.f / l_run;
+    // normalise; fold in the running result over earlier keys if there is one (each element is
+    // read, then written, by this thread: o may alias run_o)
+    float lse_out = (m_run + log2f(l_run)) * kLn2, wc = 1.f / l_run, wr = 0.f;
+    const float* rp = nullptr;
+    if (a.run_lse) {
+        const int64_t rrow = (int64_t)bh * a.Sq + qrow;
+        rp = a.run_o + rrow * D + part * DQ;
+        lse_out = fold_weights(lse_out, a.run_lse[rrow], wc, wr);
+        wc /= l_run;
+    }
     float* op = (float*)a.o + b * a.os.b + h * a.os.h + (int64_t)qrow * a.os.s + part * DQ;
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) op[d] = o[d] * inv_l;
-    if (part == 0) a.lse[(int64_t)bh * a.Sq + qrow] = (m_run + log2f(l_run)) * kLn2;
+    for (int d = 0; d < DQ; ++d) op[d] = rp ? o[d] * wc + wr * rp[d] : o[d] * wc;
+    if (part == 0) a.lse[(int64_t)bh * a.Sq + qrow] = lse_out;
 }
 
 template <int D>

@@ -36,6 +36,7 @@
 // Loads, LDS swizzles, the tile ring and the loop barrier follow the bf16 kernel.
 #include "kernels.h"
 
+#include <atomic>
 #include <math.h>
 #include <stddef.h>
 
@@ -105,6 +106,27 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// 2^x for x <= 0, clamped to [0, 1] by the exponential instruction itself (the clamp folds into
+// v_exp_f32), which also maps NaN to 0: a NaN query row (every score NaN) then adds nothing to
+// the row-sum MFMA, whose zero entries would otherwise carry the NaN into the sum of the query
+// that shares its MFMA column.  The NaN still reaches the row's own output through its
+// reference (see the lazy rescale).
+__device__ __forceinline__ float weight_exp2(float x) {
+    return __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x), 0.f, 1.f);
+}
+// E4M3 codes of 2^8 a and 2^8 b into the low (HI false) or high 16 bits of `word`, keeping the
+// other half: the scaled conversion divides by its scale operand, 2^-8 (exact).  Written as
+// assembly because the compiler's form of this conversion does not keep the other half of the
+// destination (it dropped the low half's conversion, measured wrong on the GPU); the result is
+// read many instructions later (the next tile's P.V), so no wait state is needed after it.
+template <bool HI>
+__device__ __forceinline__ void pack_e4m3_x256(int& word, float a, float b) {
+    const float inv = 1.f / 256.f;
+    if constexpr (HI)
+        asm volatile("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3 op_sel:[0,0,0,1]" : "+v"(word) : "v"(a), "v"(b), "s"(inv));
+    else
+        asm volatile("v_cvt_scalef32_pk_fp8_f32 %0, %1, %2, %3" : "+v"(word) : "v"(a), "v"(b), "s"(inv));
+}
 
 __device__ __forceinline__ void half_pair(float x, float& a, float& b) {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -138,19 +160,25 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int num_records) {
     r.w[3] = 0x00020000;
     return r;
 }
+// Resource of one tile: the bytes [off, end) of a head's data, rebased to off (empty when off >=
+// end).  The raw-buffer range check applies to the per-lane offset, not to a scalar offset, so
+// each tile gets a resource of its own and rows past the data read as zeros.
+__device__ __forceinline__ Rsrc tile_rsrc(const void* base, int off, int end) {
+    return make_rsrc((const unsigned char*)base + off, off < end ? end - off : 0);
+}
 
 // Wave-wide 16-byte-per-lane loads into consecutive 1 KiB LDS blocks (see the bf16 kernel for
 // why these are assembly: the kernel orders the LDS writes itself, by a vmcnt wait and the
 // loop barrier).
 template <int NB>
-__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB], int soff) {
+__device__ __forceinline__ void lds_dma(const Rsrc& rs, unsigned dst, const int (&goff)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
         asm volatile(
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %0, %1, %2 offen lds"
+            "buffer_load_dwordx4 %0, %1, 0 offen lds"
             :
-            : "v"(goff[i]), "s"(rs.w), "s"(soff), "{m0}"(dst + i * 1024u)
+            : "v"(goff[i]), "s"(rs.w), "{m0}"(dst + i * 1024u)
             : "memory");
 }
 
@@ -219,7 +247,7 @@ struct Wave {
 
 struct Soft {
     float mt[11];
-    float m_new, alpha, nb;  // nb = kPShift - m_new
+    float m_new, alpha, nb;  // nb = kPShift - 8 - m_new
     float x[16][2];
     float e[16][2];
 };
@@ -244,14 +272,17 @@ __device__ __forceinline__ void pair_stages(float c, Soft& sm, const f32x16_t (&
             sm.x[J][1] = __builtin_fmaf(x1, c, sm.nb);
             pin(sm.x[J][0], sm.x[J][1]);
         } else if constexpr (POS == a + 1) {
-            sm.e[J][0] = fast_exp2(sm.x[J][0]);
-            sm.e[J][1] = fast_exp2(sm.x[J][1]);
+            sm.e[J][0] = weight_exp2(sm.x[J][0]);
+            sm.e[J][1] = weight_exp2(sm.x[J][1]);
             pin(sm.e[J][0], sm.e[J][1]);
         } else if constexpr (POS == a + 2) {
-            // bytes 2J, 2J+1 of the operand: half (J & 1) of dword J / 2.  The conversion keeps
-            // the other half of the dword it is given; for the low half that is a stale value
-            // the high half's conversion then replaces (no zeroing needed)
-            p[J >> 1] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(sm.e[J][0], sm.e[J][1], (unsigned)p[J >> 1], (J & 1) != 0);
+            // bytes 2J, 2J+1 of the operand: half (J & 1) of dword J / 2, E4M3 of 2^8 times the
+            // weights (the scaled conversion divides by its scale operand, 2^-8: exact).  The
+            // conversion keeps the other half of the dword it is given; for the low half that is a
+            // stale value the high half's conversion then replaces (no zeroing needed)
+            int word = p[J >> 1];
+            pack_e4m3_x256<(J & 1) != 0>(word, sm.e[J][0], sm.e[J][1]);
+            p[J >> 1] = word;
         }
         pair_stages<POS, J + 1>(c, sm, s, p);
     }
@@ -273,13 +304,15 @@ __device__ __forceinline__ void softmax_slot(Wave& w, Soft& sm, const f32x16_t (
                               vmax(sm.mt[9], sm.mt[10]));
         float m0, m1;
         half_pair(mx, m0, m1);
-        // lazy rescale: the reference moves only when the row max exceeds it by > kRescale,
-        // so p <= 2^kRescale and 2^kPShift p fits E4M3; lanes l and l+32 agree
+        // lazy rescale: the reference moves only when the row max exceeds it by > kRescale (or
+        // is NaN: then the reference, the rescale factor and so the row's output become NaN), so
+        // p <= 2^kRescale and 2^kPShift p fits E4M3; lanes l and l+32 agree.  The exponentials
+        // give 2^(kPShift - 8) p <= 1 (see weight_exp2), and the E4M3 conversion scales by 2^8
         const float m_tile = vmax(m0, m1) * w.c;
-        sm.m_new = m_tile > w.m_run + kRescale ? m_tile : w.m_run;
+        sm.m_new = !(m_tile <= w.m_run + kRescale) ? m_tile : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
-        sm.nb = kPShift - sm.m_new;
+        sm.nb = (kPShift - 8.f) - sm.m_new;
     }
     pair_stages<POS>(w.c, sm, s, p);
 }
@@ -391,17 +424,18 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         const kernarg_t<Fp8Args>* ap = (const kernarg_t<Fp8Args>*)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
         const kernarg_t<Fp8Args>& ar = *ap;
+        const int bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
         int lane = tid & 63;
         asm volatile("" : "+v"(lane));
         const int hi = lane >> 5;
         int sk_w = -1, gidx, g_first, nkt;
-        if (ar.sk_wgs == 0 || (int)blockIdx.x < ar.n_dp) {
+        if (ar.sk_wgs == 0 || bid < ar.n_dp) {
             if (seg > 0) break;
-            gidx = xcd_remap(blockIdx.x, ar.sk_wgs == 0 ? n_q : ar.n_dp);
+            gidx = xcd_remap(bid, ar.sk_wgs == 0 ? n_q : ar.n_dp);
             g_first = 0;
             nkt = n_kt;
         } else {
-            sk_w = xcd_remap(blockIdx.x - ar.n_dp, ar.sk_wgs);
+            sk_w = xcd_remap(bid - ar.n_dp, ar.sk_wgs);
             const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             const int64_t cut = (u0 / n_kt + 1) * n_kt;
@@ -455,8 +489,8 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
 
         // tile loads: K rows through a per-lane swizzled offset, V^T tiles verbatim
         const int k_rs = (int)ar.ks.s;  // bytes per K row step
-        const Rsrc krs = make_rsrc(kp, (Skv - 1) * k_rs + D);
-        const Rsrc vrs = make_rsrc((const unsigned char*)ar.vt + (int64_t)bh * n_kt * TILE, n_kt * TILE);
+        const int k_end = (Skv - 1) * k_rs + D;  // bytes of a head's K rows
+        const unsigned char* const vtp = (const unsigned char*)ar.vt + (int64_t)bh * n_kt * TILE;
         int k_goff[BLKS_PER_WAVE], v_goff[BLKS_PER_WAVE];
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
@@ -470,10 +504,14 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         auto kbuf = [&](int t) { return (unsigned)((t % NSTAGE) * TILE); };
         auto vbuf = [&](int t) { return (unsigned)((NSTAGE + t % NSTAGE) * TILE); };
         auto load_k = [&](int g) {
-            if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(krs, kbuf(g) + wave * BLKS_PER_WAVE * 1024, k_goff, (g_first + g) * BK * k_rs);
+            if (wave < LOADERS)
+                lds_dma<BLKS_PER_WAVE>(tile_rsrc(kp, (g_first + g) * BK * k_rs, k_end),
+                                       kbuf(g) + wave * BLKS_PER_WAVE * 1024, k_goff);
         };
         auto load_v = [&](int g) {
-            if (wave < LOADERS) lds_dma<BLKS_PER_WAVE>(vrs, vbuf(g) + wave * BLKS_PER_WAVE * 1024, v_goff, (g_first + g) * TILE);
+            if (wave < LOADERS)
+                lds_dma<BLKS_PER_WAVE>(tile_rsrc(vtp, (g_first + g) * TILE, n_kt * TILE),
+                                       vbuf(g) + wave * BLKS_PER_WAVE * 1024, v_goff);
         };
 
         // per-lane operand offsets
@@ -667,14 +705,16 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
         blocks = (int64_t)a.n_dp + a.sk_wgs;
     }
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-    static bool attr_set[64] = {};
+    // per device: the kernel's dynamic LDS limit has been raised (an atomic flag, so that
+    // first calls from several threads are safe: each may set the attribute, which is idempotent)
+    static std::atomic<bool> attr_set[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    if (dev < 0 || dev >= 64 || !attr_set[dev].load(std::memory_order_acquire)) {
         e = hipFuncSetAttribute((const void*)fwd_fp8_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
         if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+        if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, stream, a, n_qt, n_kt);
     return hipGetLastError();

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace lsdit {
@@ -46,7 +47,44 @@ struct FwdArgs {
     int sk_wgs;          // 0 = no stream-K tail
     float* sk_o;
     float* sk_lse;
+    // Running result over earlier keys (the ring's online merge done in the epilogue): when
+    // run_lse is set, the output written is the LSE merge (fold_weights) of this launch's result
+    // with run_o [B, H, Sq, D] fp32 contiguous / run_lse [B, H, Sq].  o and lse may alias them
+    // (o fp32 with contiguous strides): every element is read before the same thread writes it.
+    // Stream-K partials are written unmerged; launch_sk_fixup folds the running result in.
+    const float* run_o;
+    const float* run_lse;
+    int wg_order;        // debug aid (wg_logical): order in which the logical workgroups are dispatched
 };
+
+// Logical workgroup of hardware workgroup `bid` of `n`: as launched (order 0), reversed (1), or
+// rotated by half the grid (2).  The result of a launch must not depend on the order; a test
+// checks that it is bitwise the same.
+__device__ __forceinline__ int wg_logical(int bid, int n, int order) {
+    if (order == 1) return n - 1 - bid;
+    if (order == 2) return (bid + n / 2) % n;
+    return bid;
+}
+
+// The LSE merge of two results over disjoint key sets, (O_c, lse_c) and (O_r, lse_r), in the
+// natural-log domain: returns the merged LSE and sets the weights, O = wc O_c + wr O_r.  A part
+// with LSE -inf (no keys) has weight 0, so merging with it is the identity; both -inf give
+// LSE -inf and weights 0 (O = 0); a NaN in either gives NaN weights and LSE.
+__device__ __forceinline__ float fold_weights(float lse_c, float lse_r, float& wc, float& wr) {
+    if (lse_c != lse_c || lse_r != lse_r) {
+        wc = wr = __builtin_nanf("");
+        return __builtin_nanf("");
+    }
+    const float m = fmaxf(lse_c, lse_r);
+    if (m == -INFINITY) {
+        wc = wr = 0.f;
+        return -INFINITY;
+    }
+    const float ec = expf(lse_c - m), er = expf(lse_r - m), s = ec + er;
+    wc = ec / s;
+    wr = er / s;
+    return m + logf(s);
+}
 
 // Query rows per query tile of the bf16 kernel, and the first unit of stream-K workgroup w.
 constexpr int kSkRows = 256;
@@ -64,6 +102,8 @@ struct SkFixupArgs {
     Strides os;
     int o_bf16;
     float* lse;          // [B, H, Sq]
+    const float* run_o;  // running result folded in as one more part (see FwdArgs), or null
+    const float* run_lse;
 };
 
 // Merge of up to kMaxMergeParts fp32 partials (contiguous [B,H,Sq,D] / [B,H,Sq]).
@@ -112,6 +152,7 @@ struct Fp8Args {
     int sk_wgs;          // 0 = no stream-K tail
     float* sk_o;
     float* sk_lse;
+    int wg_order;        // as in FwdArgs
 };
 int fp8_key_tiles(int Skv);
 

@@ -17,7 +17,10 @@
 // non-temporal accesses keep them from displacing other data in the caches (measured 5.4 ->
 // 5.8 TB/s for 8 parts of 44,160 x 16 rows).
 // Parts whose LSE is -inf carry no weight; if all are -inf the output is
-// O = 0, LSE = -inf.
+// O = 0, LSE = -inf.  A NaN LSE in any part (a NaN query row, or a NaN key,
+// makes its chunk's LSE NaN) makes the row's O and LSE NaN, as attention over
+// all the keys in one pass gives: the running maximum below ignores NaN, so a
+// flag carries it.
 #include "kernels.h"
 
 #include <math.h>
@@ -65,13 +68,17 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     // LSE of the union, natural-log domain (so that a single live part gets weight
     // exp(0) = 1 and passes through exactly): running max M and sum of exp(LSE_c - M)
     float M = -INFINITY, tot = 0.f;
+    bool nan = false;
     for (int c0 = 0; c0 < n; c0 += kBatch) {
         float l[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) l[u] = c0 + u < n ? a.lse_parts[c0 + u][row] : -INFINITY;
         float mb = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, l[u]);
+        for (int u = 0; u < kBatch; ++u) {
+            mb = fmaxf(mb, l[u]);
+            nan |= l[u] != l[u];
+        }
         if (mb == -INFINITY) continue;  // nothing live in this batch
         const float m_new = fmaxf(M, mb);
         float sb = 0.f;
@@ -99,6 +106,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
         }
         lse_out = L;
     }
+    if (nan) {
+        acc = f32x4_t{NAN, NAN, NAN, NAN};
+        lse_out = NAN;
+    }
     store4(a.o, a.os, a.o_bf16, a.H, a.Sq, row, d, acc);
     // lse_parts[0] may alias lse: this store depends on every load of it above.
     if (d == 0) a.lse[row] = lse_out;
@@ -125,14 +136,23 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     const int64_t t0 = (int64_t)j * a.T, t1 = t0 + a.T;
     const int w0 = (int)(((t0 + 1) * P - 1) / U);
 
+    // a running result over earlier keys, if given, is one more part (row bh*Sq + s of run_o)
+    const int64_t orow = (int64_t)bh * a.Sq + s;
+    const float l_run = a.run_lse ? a.run_lse[orow] : -INFINITY;
     float M = -INFINITY, tot = 0.f;
+    bool nan = l_run != l_run;
+    if (l_run != -INFINITY && !nan) {
+        M = l_run;
+        tot = 1.f;
+    }
     for (int w = w0; w < P; ++w) {
         const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
         if (u0 >= t1) break;
         if (u1 == u0) continue;
         const int slot = 2 * w + (u0 < t0 ? 1 : 0);
         const float l = a.sk_lse[(int64_t)slot * kSkRows + r];
-        if (l == -INFINITY) continue;
+        nan |= l != l;
+        if (l == -INFINITY || l != l) continue;
         const float m_new = fmaxf(M, l);
         tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
         M = m_new;
@@ -141,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     float lse_out = -INFINITY;
     if (M != -INFINITY) {
         const float L = M + logf(tot);
+        if (l_run != -INFINITY) acc = expf(l_run - L) * *(const f32x4_t*)(a.run_o + orow * a.D + d);
         for (int w = w0; w < P; ++w) {
             const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
             if (u0 >= t1) break;
@@ -151,8 +172,13 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
         }
         lse_out = L;
     }
-    store4(a.o, a.os, a.o_bf16, a.H, a.Sq, (int64_t)bh * a.Sq + s, d, acc);
-    if (d == 0) a.lse[(int64_t)bh * a.Sq + s] = lse_out;
+    if (nan) {
+        acc = f32x4_t{NAN, NAN, NAN, NAN};
+        lse_out = NAN;
+    }
+    // o and lse may alias run_o and run_lse: these stores depend on every load of them above
+    store4(a.o, a.os, a.o_bf16, a.H, a.Sq, orow, d, acc);
+    if (d == 0) a.lse[orow] = lse_out;
 }
 
 __global__ __launch_bounds__(kThreads) void fill_empty_kernel(void* o, Strides os, int o_bf16, float* lse, int H,

@@ -134,10 +134,13 @@ def test_shard_fwd_argument_errors(attn):
     assert _shard(lib, order=(1, -1)) == SHAPE
     assert _shard(lib, flags=0) == UNSUP
     assert _shard(lib, flags=3) == UNSUP
-    for flags in (1, 2):  # n-way and online keep fp32 partials in the workspace
+    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4  # room for the balanced tail (2 x 1 query tiles)
+    for flags, n_slots in ((1, 2), (2, 1)):  # n-way and online keep fp32 partials in the workspace
         assert _shard(lib, ws=None, flags=flags) == WS
         need = lib.attn_shard_workspace_size(1, 2, 10, 128, 2, flags)
-        assert _shard(lib, ws_bytes=need - 1, flags=flags) == WS
+        slots = need - tail  # the chunk slots are required, the tail's room is optional
+        assert slots == n_slots * (-(-20 * 128 * 4 // 256) * 256 + -(-20 * 4 // 256) * 256)
+        assert _shard(lib, ws_bytes=slots - 1, flags=flags) == WS
         assert _shard(lib, ws=P + 8, ws_bytes=need, flags=flags) == ALIGN
     assert _shard(lib, D=80) == UNSUP
     assert _shard(lib, q=None) == NULL
@@ -149,13 +152,15 @@ def test_workspace_sizes(attn):
     lib = attn.load()
     rows = 1 * 16 * 5520
     slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot   # n-way
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 2 * slot   # online
     # fused: no chunk partials.  A shape whose query tiles of 256 rows leave the last round of
     # the GPU's CUs part-full (16 heads x 22 tiles = 352 on 256 CUs; the CPU build assumes 256)
     # gets room for the balanced tail: 2 slots of 256 rows x (D + 1) fp32 per CU, whatever the
-    # chunking; a shape filling whole rounds (16 x 16 tiles) none
+    # chunking; a shape filling whole rounds (16 x 16 tiles) none.  n-way keeps every chunk's
+    # fp32 partial and online one running result, followed by the same room for the tail (each
+    # chunk's launch may run one).
     tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot + tail   # n-way
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 1 * slot + tail   # online
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == tail
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == tail  # one chunk: same kernel
     assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == tail  # 2768 tiles: 208 in the last round

@@ -186,3 +186,40 @@ def test_fp8_full_size_sampled_rows(name):
     o, l = _run(inp, w.scale)
     rows = workloads.sample_rows(w.Sq, boundaries=(256, 5520), n_random=24, seed=1)
     check_fp8(o, l, inp, w.scale, rows=rows, what="fp8 %s (%d rows x %d heads)" % (name, len(rows), w.H))
+
+
+@pytest.mark.parametrize("Skv", [1000, 63])
+def test_fp8_rows_past_the_keys_are_not_read(Skv):
+    """K and V are views of the first Skv rows of longer buffers whose rows past Skv hold the E4M3
+    NaN code, and the workspace past the V^T tiles holds it too: the last, partial key tile and
+    the tiles fetched past the end read zeros there, so the result stays finite and within the
+    bound.  (No balanced tail at this shape: the last head's V^T tiles end where the filled
+    excess of the workspace begins.)"""
+    B, H, Sq, D = 1, 2, 300, 128
+    inp = _quantized(B, H, Sq, Skv, seed=9)
+    pad = 320
+    kb = np.full((B, H, Skv + pad, D), 0x7F, np.uint8)
+    vb = np.full((B, H, Skv + pad, D), 0x7F, np.uint8)
+    kb[:, :, :Skv] = inp["k"]
+    vb[:, :, :Skv] = inp["v"]
+    q = _codes_to_device(inp["q"])
+    k, v = _codes_to_device(kb)[:, :, :Skv], _codes_to_device(vb)[:, :, :Skv]
+    need = A().fp8_workspace_size(B, H, Sq, Skv, D)
+    assert need == B * H * -(-Skv // 64) * 8192  # V^T tiles only: no tail
+    ws = torch.full((need + 65536,), 0x7F, dtype=torch.uint8, device="cuda")
+    o, l = A().chunk_fwd_fp8(q, k, v, inp["q_descale"], inp["k_descale"], inp["v_descale"], 0.1, workspace=ws)
+    torch.cuda.synchronize()
+    check_fp8(o, l, inp, 0.1, what="fp8 NaN codes past Skv=%d" % Skv)
+
+
+def test_fp8_nan_query_row_stays_in_its_row():
+    """A NaN code in one query row makes that row's O and LSE NaN and leaves every other row within
+    the bound: the row-sum MFMA's zero entries must not carry the NaN into the query sharing its
+    column (the weights are clamped to [0, 1], NaN to 0, before the E4M3 conversion)."""
+    inp = _quantized(1, 1, 64, 700, seed=10)
+    q = inp["q"].copy()
+    q[0, 0, 17, 5] = 0x7F
+    o, l = _run(dict(inp, q=q), 0.1, torch.float32)
+    assert torch.isnan(o[0, 0, 17]).all() and torch.isnan(l[0, 0, 17])
+    keep = [r for r in range(64) if r != 17]
+    check_fp8(o, l, inp, 0.1, rows=keep, what="fp8 NaN query row, other rows")

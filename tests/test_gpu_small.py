@@ -331,3 +331,120 @@ def test_noop_and_nonfinite_inputs():
     o, l = A().chunk_fwd(to_device(q), to_device(k), to_device(v), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.isnan(o[0, 0, :, 7]).all() and torch.isfinite(l).all()
+
+
+@pytest.mark.parametrize("mode", ["fused", "online", "nway"])
+def test_nan_query_row_every_schedule(mode):
+    """A NaN in one query row makes every score of that row NaN, so its O and LSE are NaN, as in
+    one pass over all keys; every other row stays finite and at parity.  One query tile against
+    79 key tiles in two chunks: the fused schedule runs it as the balanced tail (the fix-up
+    merges some 80 partials per row), and the online and n-way schedules merge per-chunk
+    partials: neither merge may turn the NaN row into the 'no keys' result O = 0, LSE = -inf."""
+    D = 128
+    q, k, v = _inputs(1, 1, 64, 5000, D, seed=12)
+    q[0, 0, 17, 5] = 0x7FC0
+    keep = [r for r in range(64) if r != 17]
+    o_ref, l_ref = oracle.attention(q[:, :, keep], k, v, 1 / math.sqrt(D))
+    o1, l1 = A().chunk_fwd(to_device(q), to_device(k), to_device(v), out_dtype=torch.float32)
+    o, l = A().shard_fwd(to_device(q), to_device(k), to_device(v), (1700, 3300), (1, 0), mode=mode,
+                         out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for oo, ll, what in ((o1, l1, "one pass"), (o, l, mode)):
+        assert torch.isnan(oo[0, 0, 17]).all() and torch.isnan(ll[0, 0, 17]), what
+        assert_parity(oo[:, :, keep], ll[:, :, keep], o_ref, l_ref, what="NaN query row, other rows, " + what)
+
+
+@pytest.mark.parametrize("Skv", [1000, 63, 5000])
+def test_rows_past_the_keys_are_not_read(Skv):
+    """K and V are views of the first Skv rows of longer buffers whose rows past Skv hold NaN.
+    The last, partial key tile and the tiles fetched past the last chunk must read those rows
+    as zeros (a NaN V row times P = 0 would poison every output): the results stay finite and
+    at parity, for one chunk and for the fused schedule with and without the balanced tail."""
+    D, B, H, Sq = 128, 1, 2, 300
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=13)
+    pad = 320  # more rows than any prefetch reaches past the end: every read stays in the buffer
+    kb = np.full((B, H, Skv + pad, D), 0x7FC0, np.uint16)
+    vb = np.full((B, H, Skv + pad, D), 0x7FC0, np.uint16)
+    kb[:, :, :Skv] = k
+    vb[:, :, :Skv] = v
+    kd, vd = to_device(kb)[:, :, :Skv], to_device(vb)[:, :, :Skv]
+    qd = to_device(q)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
+    lens = (Skv // 3, Skv - Skv // 3)
+    runs = [("chunk", lambda: A().chunk_fwd(qd, kd, vd)),
+            ("fused", lambda: A().shard_fwd(qd, kd, vd, lens, (1, 0), mode="fused")),
+            ("fused, no workspace", lambda: A().shard_fwd(qd, kd, vd, lens, (1, 0), mode="fused",
+                                                          workspace=torch.empty(0, dtype=torch.uint8,
+                                                                                device="cuda")))]
+    for what, fn in runs:
+        o, l = fn()
+        torch.cuda.synchronize()
+        assert_parity(o, l, o_ref, l_ref, what="NaN rows past Skv=%d, %s" % (Skv, what))
+
+
+def test_side_stream_with_allocations_on_the_current_stream():
+    """shard_fwd on a side stream allocates its workspace and outputs on the current stream; the
+    binding records their use on the side stream, so buffers the current stream allocates and
+    fills meanwhile never reuse that memory while the kernels still write it."""
+    D, B, H, Sq, Skv = 128, 1, 3, 600, 9000
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=14)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D), q_rows=[0, 299, 599])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    results = []
+    for mode in ("online", "fused", "nway"):
+        o, l = A().shard_fwd(qd, kd, vd, (3000, 6000), (1, 0), mode=mode, stream=side)
+        results.append((mode, o, l))
+        # the current stream allocates and fills memory while the side stream still runs
+        junk = [torch.full((1 << 22,), float("nan"), device="cuda") for _ in range(8)]
+        del junk
+    torch.cuda.synchronize()
+    for mode, o, l in results:
+        assert_parity(o[:, :, [0, 299, 599]], l[:, :, [0, 299, 599]], o_ref, l_ref, what="side stream " + mode)
+
+
+def test_determinism_through_the_balanced_tail():
+    """A fixed plan is bitwise repeatable on the tail path too: runs of key tiles, their fp32
+    partials and the fix-up's merge order are fixed (no atomics)."""
+    D, B, H, Sq, Skv = 128, 1, 20, 3600, 5000
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=15)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    assert A().shard_workspace_size(B, H, Sq, D, 2, "fused") > 0
+    o, l = A().shard_fwd(qd, kd, vd, (2000, 3000), (1, 0), mode="fused", out_dtype=torch.float32)
+    for _ in range(3):
+        o2, l2 = A().shard_fwd(qd, kd, vd, (2000, 3000), (1, 0), mode="fused", out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(l, l2)
+
+
+@pytest.mark.parametrize("order", ["reverse", "rotate"])
+def test_workgroup_order_does_not_change_results(order, monkeypatch):
+    """Dispatching the forward kernels' logical workgroups in another order (the library's debug
+    aid LSDIT_DEBUG_WG_ORDER: reversed, or rotated by half the grid) gives bitwise the same O and
+    LSE: whole query tiles and the balanced tail's runs write disjoint rows and slots, nothing is
+    accumulated across workgroups, and the fix-up merges in a fixed order.  The fused schedule
+    with the tail (300 query tiles: 256 whole, 44 as runs), the per-chunk schedules, and the FP8
+    variant with its tail."""
+    D, B, H, Sq, Skv = 128, 1, 20, 3600, 5000
+    q, k, v = _inputs(B, H, Sq, Skv, D, seed=16)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    x8 = {n: synth.e4m3_quantize(synth.normal_rows(17, i, 1, 3, 200, D, kind=synth.KIND_F32))
+          for i, n in enumerate("qkv")}
+    c8 = {n: torch.from_numpy(x8[n][0]).cuda() for n in "qkv"}
+
+    def runs():
+        out = []
+        for mode in ("fused", "online", "nway"):
+            out.append(A().shard_fwd(qd, kd, vd, (2000, 3000), (1, 0), mode=mode, out_dtype=torch.float32))
+        out.append(A().chunk_fwd_fp8(c8["q"], c8["k"], c8["v"], x8["q"][1], x8["k"][1], x8["v"][1], 0.1,
+                                     out_dtype=torch.float32))
+        torch.cuda.synchronize()
+        return out
+
+    monkeypatch.delenv("LSDIT_DEBUG_WG_ORDER", raising=False)
+    ref = runs()
+    monkeypatch.setenv("LSDIT_DEBUG_WG_ORDER", order)
+    got = runs()
+    for (o, l), (o2, l2), what in zip(ref, got, ("fused", "online", "nway", "fp8")):
+        assert torch.equal(o, o2) and torch.equal(l, l2), "%s, order %s" % (what, order)
