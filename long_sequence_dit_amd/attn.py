@@ -17,7 +17,10 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# LSDIT_ATTN_LIBRARY selects another build of the same sources (the sanitizer test loads the
+# AddressSanitizer build of the host code this way).
+_LIB_PATH = os.environ.get("LSDIT_ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                                 "libattn.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -122,6 +125,25 @@ def _stream_ptr(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _side_stream(stream):
+    """The torch stream a call runs on when that is not the current stream (else None)."""
+    if stream is None:
+        return None
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    return None if s.cuda_stream == torch.cuda.current_stream().cuda_stream else s
+
+
+def _used_on(stream, *tensors):
+    """Tensors this binding allocated (on the current stream) for a call enqueued on another
+    stream: tell the caching allocator that stream uses them, so that their memory is not handed
+    to a later allocation before the call's kernels are done with it."""
+    s = _side_stream(stream)
+    if s is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+
+
 def _scale(scale, D):
     return float(1.0 / math.sqrt(D) if scale is None else scale)
 
@@ -135,12 +157,16 @@ def chunk_fwd(q, k, v, scale=None, out=None, lse=None, out_dtype=None, stream=No
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share a dtype")
     out_dtype = out_dtype or q.dtype
+    own = []
     if out is None:
         out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
+        own.append(out)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        own.append(lse)
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise ValueError("lse must be contiguous fp32 [B, H, Sq]")
+    _used_on(stream, *own)
     rc = load().attn_chunk_fwd(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),
                                _bhsd(v, "v"), _dt(q), B, H, Sq, Skv, D, _scale(scale, D), out.data_ptr(),
                                _bhsd(out, "out"), _dt(out), lse.data_ptr(), _stream_ptr(stream))
@@ -169,15 +195,20 @@ def chunk_fwd_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
     Skv = k.shape[2]
     if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
         raise ValueError("k, v must be [B, H, Skv, D] matching q")
+    own = []
     if out is None:
         out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
+        own.append(out)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        own.append(lse)
     if not lse.is_contiguous() or lse.dtype != torch.float32:
         raise ValueError("lse must be contiguous fp32 [B, H, Sq]")
     need = fp8_workspace_size(B, H, Sq, Skv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        own.append(workspace)
+    _used_on(stream, *own)
     rc = load().attn_chunk_fwd_fp8(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),
                                    _bhsd(v, "v"), float(q_descale), float(k_descale), float(v_descale), B, H, Sq,
                                    Skv, D, _scale(scale, D), workspace.data_ptr(), workspace.numel(),
@@ -200,10 +231,14 @@ def lse_merge(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor]
             raise ValueError("lse parts must be contiguous fp32 [B, H, Sq]")
         if not o_.is_cuda or not l_.is_cuda:
             raise ValueError("parts must be GPU tensors")
+    own = []
     if out is None:
         out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=o_parts[0].device)
+        own.append(out)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=o_parts[0].device)
+        own.append(lse)
+    _used_on(stream, *own)
     optr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in o_parts])
     lptr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in lse_parts])
     rc = load().attn_lse_merge(n, optr, lptr, B, H, Sq, D, out.data_ptr(), _bhsd(out, "out"), _dt(out),
@@ -231,15 +266,20 @@ def shard_fwd(q, k, v, chunk_lens: Sequence[int], order: Optional[Sequence[int]]
     ordp = None if order is None else (ctypes.c_int32 * max(len(order), 1))(*[int(x) for x in order])
     flags = _MODES[mode]
     need = shard_workspace_size(B, H, Sq, D, n, mode) if n >= 1 else 0
+    own = []
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        own.append(workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     out_dtype = out_dtype or q.dtype
     if out is None:
         out = torch.empty((B, H, Sq, D), dtype=out_dtype, device=q.device)
+        own.append(out)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        own.append(lse)
+    _used_on(stream, *own)
     rc = load().attn_shard_fwd(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),
                                _bhsd(v, "v"), _dt(q), B, H, Sq, D, _scale(scale, D), n, lens, ordp, flags, ws_ptr,
                                ws_bytes, out.data_ptr(), _bhsd(out, "out"), _dt(out), lse.data_ptr(),
@@ -255,6 +295,7 @@ def ulysses_pack(x, n: int, packed=None, stream=None):
         raise ValueError("H must be a multiple of n")
     if packed is None:
         packed = torch.empty((n, S, B, H // n, D), dtype=x.dtype, device=x.device)
+        _used_on(stream, packed)
     if not packed.is_contiguous() or packed.dtype != x.dtype or tuple(packed.shape) != (n, S, B, H // n, D):
         raise ValueError("packed must be contiguous [n, S, B, H/n, D] of x's dtype")
     rc = load().attn_ulysses_pack(x.data_ptr(), _bhsd(x, "x"), _dt(x), B, H, S, D, n, packed.data_ptr(),
@@ -270,6 +311,7 @@ def ulysses_unpack(packed, out=None, stream=None):
         raise ValueError("packed must be contiguous")
     if out is None:
         out = torch.empty((B, n * Hg, S, D), dtype=packed.dtype, device=packed.device)
+        _used_on(stream, out)
     if tuple(out.shape) != (B, n * Hg, S, D) or out.dtype != packed.dtype:
         raise ValueError("out must be [B, n*Hg, S, D] of packed's dtype")
     rc = load().attn_ulysses_unpack(packed.data_ptr(), _dt(packed), B, n * Hg, S, D, n, out.data_ptr(),

@@ -50,6 +50,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+LIB_SAN = os.path.join(PKG, "libattn_san.so")
+SAN_OBJDIR = os.path.join(PKG, "_build_san")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """libattn_san.so: the host code of the C ABI (argument checks, chunk plan, workspace layout,
+    shard driver) built with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the
+    kernels' objects as built by build().  For the CPU sanitizer test, which loads it into a
+    process whose AddressSanitizer runtime is preloaded.  The sanitizers apply to host code only:
+    every -fsanitize flag is given to the host compilation alone (-Xarch_host)."""
+    if not all(os.path.exists(os.path.join(OBJDIR, os.path.splitext(f)[0] + ".o")) for f in SOURCES):
+        build(verbose)
+    os.makedirs(SAN_OBJDIR, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    api_obj = os.path.join(SAN_OBJDIR, "attn_api.o")
+    cmd = [HIPCC] + COMMON + san + ["-x", "hip", "-c", os.path.join(CSRC, "attn_api.cpp"), "-o", api_obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for the sanitized attn_api.cpp:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    objs = [api_obj] + [os.path.join(OBJDIR, os.path.splitext(f)[0] + ".o") for f in SOURCES if f != "attn_api.cpp"]
+    tmp = LIB_SAN + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-shared-libsan", "-o", tmp] + objs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, LIB_SAN)
+    if verbose:
+        print("built", LIB_SAN)
+    return LIB_SAN
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)

@@ -33,23 +33,35 @@ _lib = None
 _KINDS = {np.dtype(np.float64): 0, np.dtype(np.float32): 1, np.dtype(np.uint16): 2}
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (IEEE fp64, no fast-math), OpenMP over query rows."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-fno-fast-math",
-                               _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile liboracle.so with gcc (IEEE fp64, no fast-math), OpenMP over query rows; with
+    sanitize, liboracle_san.so instead (clang, AddressSanitizer + UndefinedBehaviorSanitizer, the
+    same source and flags otherwise), for the sanitizer test."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        if sanitize:
+            import synth
+            cmd = ["/opt/rocm/llvm/bin/clang"] + synth.SANITIZE_FLAGS + [
+                "-fopenmp", "-fPIC", "-shared", "-std=c11", "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
+            path = os.environ.get("ORACLE_LIBRARY") or _LIB  # another build of the same source
+            if path == _LIB and not os.path.exists(_LIB):
                 build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(path)
             i64, vp, dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
             lib.oracle_attention.argtypes = [i64] * 5 + [dbl, vp, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int,
                                                         i64, i64, vp, vp, vp, ctypes.c_int]

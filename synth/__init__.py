@@ -26,24 +26,36 @@ KIND_F64, KIND_F32, KIND_BF16 = 0, 1, 2
 TID_Q, TID_K, TID_V, TID_OUTLIER = 0, 1, 2, 3
 
 
-def build(force: bool = True) -> str:
-    """Compile libsynth.so next to its source (plain gcc, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
-        )
-        os.replace(tmp, _LIB)
-    return _LIB
+_LIB_SAN = os.path.join(_HERE, "libsynth_san.so")
+# clang of the ROCm toolchain, whose AddressSanitizer runtime the sanitized HIP library uses too
+_CLANG = "/opt/rocm/llvm/bin/clang"
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-shared-libsan",
+                  "-Wl,-rpath,/opt/rocm/llvm/lib"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile libsynth.so next to its source (plain gcc, OpenMP); with sanitize, libsynth_san.so
+    instead (clang, AddressSanitizer + UndefinedBehaviorSanitizer), for the sanitizer test."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = [_CLANG] + SANITIZE_FLAGS + ["-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB):
+            path = os.environ.get("SYNTH_LIBRARY") or _LIB  # another build of the same source
+            if path == _LIB and not os.path.exists(_LIB):
                 build(force=False)
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(path)
             lib.synth_philox4x32_10.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_uint32)]
             lib.synth_philox4x32_10.restype = None
             lib.synth_raw_u32.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_uint64,
