@@ -31,9 +31,11 @@
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
  *    the legacy default stream).  Nothing is synchronised by the library.
  *  - The caller owns every buffer.  The library allocates no device memory
- *    and is re-entrant.  It keeps no state from one call to the next beyond
- *    what it sets up once per device, thread-safely: that a kernel's LDS
- *    size attribute is set.
+ *    (apart from the static scratch array of attn_shard_fwd_noalloc, part of
+ *    the library's code object) and is re-entrant.  It keeps no state from
+ *    one call to the next beyond what it sets up once per device, thread-
+ *    safely: that a kernel's LDS size attribute is set, and the scratch
+ *    array's device address.
  *  - Arguments are checked before anything is launched.  A non-OK status
  *    means nothing was enqueued and no output was touched, except
  *    ATTN_ERR_HIP, which reports a failed launch (a later kernel fault shows
@@ -189,6 +191,37 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
                              float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
                              uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
                              attn_dtype_t o_dt, float* lse, attn_stream_t stream);
+
+/*
+ * attn_shard_fwd_noalloc — attn_shard_fwd with the ATTN_MERGE_FUSED schedule
+ * and no workspace argument, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc.  It calls no hipMalloc, hipFree or other allocating routine.
+ *
+ * The balanced tail's fp32 partials (see attn_shard_fwd) go to a scratch
+ * array in the library's static device memory instead of a workspace:
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes (2 * 256 * 256 * (128 + 1) fp32 values,
+ * 64.5 MiB) on each device the library runs on, held until the process ends.
+ * The tail's plan spreads over at most 256 workgroups, so the need never
+ * exceeds it for D <= 128; a shape that would need more is rejected with
+ * ATTN_ERR_WORKSPACE before anything is launched.
+ *
+ * The first call on a device looks up that device's copy of the array (the
+ * set-up; a caller that captures graphs makes one call before capturing).
+ * Every call on a device shares its one array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * device (two streams, or two threads) race on it and must be serialised by
+ * the caller.  Arguments, results and errors are those of attn_shard_fwd with
+ * flags = ATTN_MERGE_FUSED; the result is bitwise that of attn_shard_fwd with
+ * a workspace of attn_shard_workspace_size() bytes on a device of at most 256
+ * CUs.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES 67633152u
+attn_status_t attn_shard_fwd_noalloc(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks,
+                                     const void* v, attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H,
+                                     int32_t Sq, int32_t D, float scale, int32_t n_chunks, const int32_t* chunk_len,
+                                     const int32_t* order, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                                     attn_stream_t stream);
 
 /*
  * attn_ulysses_pack / attn_ulysses_unpack — the local halves of the all-to-all

@@ -34,7 +34,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_DT
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_chunk_fwd", "attn_lse_merge", "attn_shard_workspace_size", "attn_shard_fwd",
-           "attn_ulysses_pack", "attn_ulysses_unpack", "attn_fp8_workspace_size", "attn_chunk_fwd_fp8",
+           "attn_shard_fwd_noalloc", "attn_ulysses_pack", "attn_ulysses_unpack", "attn_fp8_workspace_size", "attn_chunk_fwd_fp8",
            "attn_status_str", "attn_abi_version")
 
 
@@ -72,6 +72,9 @@ def load():
         lib.attn_shard_fwd.argtypes = [vp, Strides, vp, Strides, vp, Strides, ctypes.c_int, i32, i32, i32, i32, f32,
                                        i32, vp, vp, u32, vp, sz, vp, Strides, ctypes.c_int, vp, vp]
         lib.attn_shard_fwd.restype = ctypes.c_int
+        lib.attn_shard_fwd_noalloc.argtypes = [vp, Strides, vp, Strides, vp, Strides, ctypes.c_int, i32, i32, i32,
+                                               i32, f32, i32, vp, vp, vp, Strides, ctypes.c_int, vp, vp]
+        lib.attn_shard_fwd_noalloc.restype = ctypes.c_int
         lib.attn_ulysses_pack.argtypes = [vp, Strides, ctypes.c_int, i32, i32, i32, i32, i32, vp, vp]
         lib.attn_ulysses_pack.restype = ctypes.c_int
         lib.attn_ulysses_unpack.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, i32, vp, Strides, vp]
@@ -285,6 +288,31 @@ def shard_fwd(q, k, v, chunk_lens: Sequence[int], order: Optional[Sequence[int]]
                                ws_bytes, out.data_ptr(), _bhsd(out, "out"), _dt(out), lse.data_ptr(),
                                _stream_ptr(stream))
     _check(rc, "attn_shard_fwd")
+    return out, lse
+
+
+def shard_fwd_noalloc(q, k, v, chunk_lens: Sequence[int], order: Optional[Sequence[int]], out, lse, scale=None,
+                      stream=None):
+    """shard_fwd with the fused schedule and no workspace: the library keeps the balanced tail's
+    partials in its static scratch array.  Allocates nothing: the caller passes `out` and `lse`."""
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError("k, v must be [B, H, Skv, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if tuple(out.shape) != (B, H, Sq, D):
+        raise ValueError("out must be [B, H, Sq, D]")
+    if tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous() or lse.dtype != torch.float32:
+        raise ValueError("lse must be contiguous fp32 [B, H, Sq]")
+    n = len(chunk_lens)
+    lens = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in chunk_lens])
+    ordp = None if order is None else (ctypes.c_int32 * max(len(order), 1))(*[int(x) for x in order])
+    rc = load().attn_shard_fwd_noalloc(q.data_ptr(), _bhsd(q, "q"), k.data_ptr(), _bhsd(k, "k"), v.data_ptr(),
+                                       _bhsd(v, "v"), _dt(q), B, H, Sq, D, _scale(scale, D), n, lens, ordp,
+                                       out.data_ptr(), _bhsd(out, "out"), _dt(out), lse.data_ptr(),
+                                       _stream_ptr(stream))
+    _check(rc, "attn_shard_fwd_noalloc")
     return out, lse
 
 

@@ -17,6 +17,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -151,15 +153,54 @@ int slots_for(uint32_t flags, int32_t n) {
 }
 
 
+// ---- the static scratch of attn_shard_fwd_noalloc: the balanced tail's partials (fp32 O, then
+// fp32 LSE, as in a workspace) of at most kScratchTailWgs workgroups at D <= 128.
+constexpr int kScratchTailWgs = 256;
+constexpr size_t kScratchBytes = ((size_t)2 * kScratchTailWgs * lsdit::kSkRows * 128 * 4 + kAlign - 1) / kAlign * kAlign +
+                                 ((size_t)2 * kScratchTailWgs * lsdit::kSkRows * 4 + kAlign - 1) / kAlign * kAlign;
+static_assert(kScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES, "2 * 256 slots of 256 rows: 128 fp32 values and an LSE each");
+
 }  // namespace
+
+// Every device holds its own copy of this array, from the library's first use on the device
+// until the process ends.  In host code `scratch` names a host-side stand-in: its device address
+// comes from hipGetSymbolAddress (scratch_address), and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
-// The shard driver behind attn_shard_fwd.
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept: the lookup is the set-up, later calls reuse the address.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::atomic<void*> addr[64];
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        static std::mutex mu;
+        std::lock_guard<std::mutex> g(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// The shard driver behind attn_shard_fwd and attn_shard_fwd_noalloc.  With `scratch` set, the
+// balanced tail's partials go to the library's static scratch array (workspace and ws_bytes are
+// then ignored) and its plan spreads over at most kScratchTailWgs workgroups.
 attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
                              attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H, int32_t Sq, int32_t D,
                              float scale, int32_t n_chunks, const int32_t* chunk_len, const int32_t* order,
-                             uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
+                             uint32_t flags, void* workspace, size_t ws_bytes, bool scratch, void* o,
+                             attn_strides_t os, attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
     // ---- chunk plan (host): lengths, offsets, processing order
     if (n_chunks < 1) return ATTN_ERR_SHAPE;
     if (n_chunks > ATTN_MAX_CHUNKS) return ATTN_ERR_UNSUPPORTED;
@@ -204,7 +245,7 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
     }
     void* tail_ws = nullptr;
     size_t tail_bytes = 0;
-    if (workspace && ws_aligned && ws_bytes > slots_need) {
+    if (!scratch && workspace && ws_aligned && ws_bytes > slots_need) {
         tail_ws = (char*)workspace + slots_need;
         tail_bytes = ws_bytes - slots_need;
     }
@@ -235,15 +276,21 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
     auto ok = [](hipError_t e) { return e == hipSuccess; };
     const int64_t n_q = n_qtiles(B, H, Sq);
     const int cus = device_cus();
+    const int tail_cus = scratch && cus > kScratchTailWgs ? kScratchTailWgs : cus;
 
     // One kernel launch over a's chunk list (T key tiles) into a's output, folding in a's running
     // result if it has one.  When its query tiles leave the last round of CUs part-full, that
     // round's work is spread evenly (the balanced tail) as far as the tail's room allows, and the
     // fix-up kernel merges the runs' partials (and the running result) into the output.
     auto launch = [&](FwdArgs a, int64_t T) -> attn_status_t {
-        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, cus, kSkMinSavingBf16) : SkPlan{};
+        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, tail_cus, kSkMinSavingBf16) : SkPlan{};
         void* tw = tail_ws;
-        const size_t tb = tail_bytes;
+        size_t tb = tail_bytes;
+        if (scratch && p.sk_wgs) {
+            if (sk_bytes(p.sk_wgs, D) > kScratchBytes) return ATTN_ERR_WORKSPACE;  // not with D <= 128
+            if (!ok(scratch_address(&tw))) return ATTN_ERR_HIP;
+            tb = kScratchBytes;
+        }
         if (p.sk_wgs == 0 || !tw || tb < sk_bytes(p.sk_wgs, D)) return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
@@ -385,7 +432,16 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
                              uint32_t flags, void* workspace, size_t ws_bytes, void* o, attn_strides_t os,
                              attn_dtype_t o_dt, float* lse, attn_stream_t stream) {
     return shard_fwd_impl(q, qs, k, ks, v, vs, in_dt, B, H, Sq, D, scale, n_chunks, chunk_len, order, flags,
-                          workspace, ws_bytes, o, os, o_dt, lse, stream);
+                          workspace, ws_bytes, false, o, os, o_dt, lse, stream);
+}
+
+attn_status_t attn_shard_fwd_noalloc(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks,
+                                     const void* v, attn_strides_t vs, attn_dtype_t in_dt, int32_t B, int32_t H,
+                                     int32_t Sq, int32_t D, float scale, int32_t n_chunks, const int32_t* chunk_len,
+                                     const int32_t* order, void* o, attn_strides_t os, attn_dtype_t o_dt, float* lse,
+                                     attn_stream_t stream) {
+    return shard_fwd_impl(q, qs, k, ks, v, vs, in_dt, B, H, Sq, D, scale, n_chunks, chunk_len, order,
+                          ATTN_MERGE_FUSED, nullptr, 0, true, o, os, o_dt, lse, stream);
 }
 
 namespace {
