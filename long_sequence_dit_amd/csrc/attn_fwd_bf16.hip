@@ -511,9 +511,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
 
     // ---- this workgroup's work: segments (query tile, run of the key-tile sequence).
     // Without a stream-K tail the grid is the B*H*n_qt query tiles, one whole tile each.  With
-    // one, workgroups below n_dp take whole query tiles (remapped over that part alone: the
-    // tail's workgroups follow in dispatch order) and the others an equal run of the tail's
-    // units, which spans at most two query tiles.
+    // one, workgroups below n_dp take whole query tiles (remapped over that part alone) and the
+    // others, which follow them in dispatch order, an equal run of the tail's units, which spans
+    // at most two query tiles.
     // Only seg is carried from one segment to the next: each iteration derives its segment from
     // the workgroup index again (state kept live across the key loop would cost registers).
     for (int seg = 0;; ++seg) {
@@ -535,7 +535,12 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             g_first = 0;
             nkt = nkt_all;
         } else {
-            sk_w = xcd_remap(bid - ar.n_dp, ar.sk_wgs);
+            // the tail's runs in plain dispatch order: the XCDs take them round-robin, so the
+            // runs on one XCD are 8 apart, whose start keys differ by 8 U / P units, often a
+            // whole number of query tiles (the ring share) or half of one (the full
+            // sequence): they stream the same key tiles together and share them in the L2
+            // (remapped to consecutive runs, their starts spread over the whole key range)
+            sk_w = bid - ar.n_dp;
             const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1

@@ -435,7 +435,12 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             g_first = 0;
             nkt = n_kt;
         } else {
-            sk_w = xcd_remap(bid - ar.n_dp, ar.sk_wgs);
+            // the tail's runs in plain dispatch order: the XCDs take them round-robin, so the
+            // runs on one XCD are 8 apart, whose start keys differ by 8 U / P units, often a
+            // whole number of query tiles (the ring share) or half of one (the full
+            // sequence): they stream the same key tiles together and share them in the L2
+            // (remapped to consecutive runs, their starts spread over the whole key range)
+            sk_w = bid - ar.n_dp;
             const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             const int64_t cut = (u0 / n_kt + 1) * n_kt;
