@@ -24,7 +24,8 @@
 //    at the matching key rows;
 //  * per 64-key tile t a wave runs one hand-ordered stream of MFMA slots:
 //    the P.V MFMAs of tile t-1, then the score MFMAs of tile t+1.  Each slot
-//    also issues the LDS read of the operand kPrefetch slots ahead, and the
+//    also issues the LDS read of the operand kPrefetch slots ahead (the last
+//    slots those of the next stream, so no stream starts on an LDS wait), and the
 //    slots carry a fixed share of the softmax of tile t: the max tree, then
 //    the probabilities as a three-stage software pipeline (FMA, exp, pack
 //    and sum in consecutive slots), so no slot holds a dependent VALU chain
@@ -300,7 +301,8 @@ __host__ __device__ constexpr int last_a_slot() {
 struct Soft {
     float mt[11];           // partial maxima
     float m0, m1;           // row max of each half of the wave
-    float m_new, alpha;
+    float m_new, alpha;     // the tile's reference; 2^(old reference - m_new) when moved
+    bool moved;             // some row's reference moved (wave-uniform)
     float x[16][2];         // stage A results (scaled, shifted scores)
     float e[16][2];         // stage B results (probabilities)
 };
@@ -379,10 +381,18 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
         // after a move), O and l share the reference (consistent), and LSE = r + log2 l.  A NaN
         // row max (a NaN score) moves the reference to NaN, which makes the rescale factor and
         // so the row's output and LSE NaN.  Lanes l and l+32 hold the same row and agree.
+        // Most tiles move no row's reference: one wave-wide test then skips the rest (the new
+        // reference, the factor 2^(r - r_new) and the rescale after the stream).
         const float m_tile = vmax(sm.m0, sm.m1) * w.c;  // max(m0, m1)
-        sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
-        sm.alpha = fast_exp2(w.m_run - sm.m_new);
-        w.m_run = sm.m_new;
+        sm.moved = __builtin_amdgcn_ballot_w64(!(m_tile <= w.m_run)) != 0;
+        if (sm.moved) {
+            asm volatile("");  // a branch, not selects computed on every tile
+            sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
+            sm.alpha = fast_exp2(w.m_run - sm.m_new);
+            w.m_run = sm.m_new;
+        } else {
+            sm.m_new = w.m_run;
+        }
     }
     pair_stages<POS, last_a_slot<D>()>(w.c, sm, s, p);
 }
@@ -420,15 +430,25 @@ __device__ __forceinline__ u32x4_t read_opnd(const Wave<D>& w, unsigned vb, unsi
 }
 
 // Slot SLOT of a stream (see stream()), then the following slots.
-template <int D, bool DO_PV, bool DO_S, bool DO_SM, int SLOT>
-__device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned kb_, u32x4_t (&ring)[kPrefetch],
-                                             const u32x4_t (&p_prev)[4], const f32x16_t (&s_cur)[2],
-                                             f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
+template <int D, bool DO_PV, bool DO_S, bool DO_SM, bool NEXT, int SLOT>
+__device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned kb_, unsigned vb_next, bool bar,
+                                             u32x4_t (&ring)[kPrefetch], const u32x4_t (&p_prev)[4],
+                                             const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], u32x4_t (&p_cur)[4],
+                                             Soft& sm) {
     using C = Cfg<D>;
     constexpr int first = DO_PV ? 0 : C::N_PV;
     constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
     if constexpr (SLOT < last) {
         constexpr int pos = SLOT - first;
+        if constexpr (NEXT && SLOT == last - kPrefetch) {
+            // the pair's barrier, before the reads of the next stream's operands: its V tile
+            // may be one this pair's loads brought in (the last MFMA operands of this stream
+            // are in registers by now: the barrier waits for every LDS read)
+            if (bar) {
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                __syncthreads();
+            }
+        }
         const u32x4_t op = ring[pos % kPrefetch];
         if constexpr (SLOT < C::N_PV) {
             constexpr int ks = SLOT / (D / 32), dt = SLOT % (D / 32);
@@ -450,10 +470,14 @@ __device__ __forceinline__ void stream_slots(Wave<D>& w, unsigned vb, unsigned k
                                                                 0, 0);
             }
         }
-        if constexpr (SLOT + kPrefetch < last) ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(w, vb, kb_);
+        if constexpr (SLOT + kPrefetch < last)
+            ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch>(w, vb, kb_);
+        else if constexpr (NEXT)  // the next stream's P.V operand SLOT + kPrefetch - last
+            ring[pos % kPrefetch] = read_opnd<D, SLOT + kPrefetch - last>(w, vb_next, 0);
         if constexpr (DO_SM && pos < last_a_slot<D>() + 3) softmax_slot<D, pos>(w, sm, s_cur, p_cur);
         __builtin_amdgcn_sched_barrier(0);
-        stream_slots<D, DO_PV, DO_S, DO_SM, SLOT + 1>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
+        stream_slots<D, DO_PV, DO_S, DO_SM, NEXT, SLOT + 1>(w, vb, kb_, vb_next, bar, ring, p_prev, s_cur, s, p_cur,
+                                                            sm);
     }
 }
 
@@ -470,20 +494,26 @@ __device__ __forceinline__ void ring_fill(const Wave<D>& w, unsigned vb, unsigne
 
 // One stream: P.V of the tile at LDS offset v0 (if DO_PV, with probabilities p_prev), the
 // softmax of the scores in s into p_cur (if DO_SM; on the P.V slots), then the scores of the
-// tile at k0 into s (if DO_S; on the later slots, after the softmax has read s).
-template <int D, bool DO_PV, bool DO_S, bool DO_SM>
-__device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, const u32x4_t (&p_prev)[4],
-                                       const f32x16_t (&s_cur)[2], f32x16_t (&s)[2], u32x4_t (&p_cur)[4], Soft& sm) {
+// tile at k0 into s (if DO_S; on the later slots, after the softmax has read s).  The operand
+// ring holds the MFMA operands read ahead: FILL reads the stream's first ones at its start;
+// otherwise the previous stream has read them.  With NEXT the stream's last slots read the
+// first operands of the next stream, a P.V stream on the V tile at v_next, and with bar (a
+// wave-uniform flag) the stream takes the pair's barrier before those reads.
+template <int D, bool DO_PV, bool DO_S, bool DO_SM, bool FILL, bool NEXT>
+__device__ __forceinline__ void stream(Wave<D>& w, int v0, int k0, unsigned v_next, bool bar, u32x4_t (&ring)[kPrefetch],
+                                       const u32x4_t (&p_prev)[4], const f32x16_t (&s_cur)[2], f32x16_t (&s)[2],
+                                       u32x4_t (&p_cur)[4], Soft& sm) {
     using C = Cfg<D>;
     static_assert(!DO_SM || (DO_PV && DO_S), "the softmax needs the full stream's slots");
     static_assert(C::N_PV >= 8 && C::N_S >= 2, "stream too short for the softmax pipeline");
     constexpr int first = DO_PV ? 0 : C::N_PV;
     constexpr int last = DO_S ? C::N_PV + C::N_S : C::N_PV;
+    // a read for the next stream's operand j lands in the ring entry that stream takes it from
+    static_assert(!NEXT || ((last - first) % kPrefetch == 0 && C::N_PV >= kPrefetch), "ring out of step");
     const unsigned vb = v0, kb_ = k0;
-    u32x4_t ring[kPrefetch];
-    ring_fill<D, DO_PV>(w, vb, kb_, ring, last);
+    if constexpr (FILL) ring_fill<D, DO_PV>(w, vb, kb_, ring, last);
     __builtin_amdgcn_sched_barrier(0);
-    stream_slots<D, DO_PV, DO_S, DO_SM, first>(w, vb, kb_, ring, p_prev, s_cur, s, p_cur, sm);
+    stream_slots<D, DO_PV, DO_S, DO_SM, NEXT, first>(w, vb, kb_, v_next, bar, ring, p_prev, s_cur, s, p_cur, sm);
 }
 
 template <int D>
@@ -700,7 +730,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // after the softmax of a tile: the rare rescale of the running output and row sums (the
         // latter with the factor of the query whose sum the lane_it holds)
         auto finish_softmax = [&]() {
-            if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
+            if (sm.moved) {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -708,8 +738,9 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                 w.lacc *= from_lane(rowsum_partner(lane_it), sm.alpha);
             }
         };
+        u32x4_t ring[kPrefetch];  // MFMA operands read ahead (see stream)
         // tile 0: scores, then its softmax on its own
-        stream<D, false, true, false>(w, vbuf(0), kbuf(0), pp, sA, sA, pp, sm);  // S_0 -> sA
+        stream<D, false, true, false, true, false>(w, vbuf(0), kbuf(0), 0, false, ring, pp, sA, sA, pp, sm);  // S_0
         mask(sA, next_valid());
         softmax_all<D>(w, sm, sA, pp);  // P_0
         finish_softmax();
@@ -722,15 +753,21 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // constant, the buffers an iteration reads are constants, which fold into the LDS reads'
         // offset fields.  (The lambdas are always inlined: as calls, the register arrays they
         // touch would go to scratch.)
+        // Each iteration's stream reads the first operands of the next one, which is the P.V of
+        // tile t (V_t, buffer P): iteration t+1's stream or, after the last iteration, the final
+        // P.V; bar: this stream ends its pair (takes the pair's barrier).
         auto body = [&](auto phase, int t, u32x4_t(&p_prev)[4], u32x4_t(&p_cur)[4], f32x16_t(&s_cur)[2],
-                        f32x16_t(&s_next)[2]) __attribute__((always_inline)) {
+                        f32x16_t(&s_next)[2], bool bar) __attribute__((always_inline)) {
             constexpr int P = decltype(phase)::value;
             constexpr unsigned k_next = ((P + 1) % C::NSTAGE) * C::TILE_BYTES;                // K_{t+1}
             constexpr unsigned v_prev = ((P + C::NSTAGE - 1) % C::NSTAGE) * C::TILE_BYTES;    // V_{t-1}
+            constexpr unsigned v_cur = P * C::TILE_BYTES;                                     // V_t
             if (t == 0) {
-                stream<D, false, true, false>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+                stream<D, false, true, false, true, true>(w, v_prev, k_next, v_cur, bar, ring, p_prev, s_cur, s_next,
+                                                          p_cur, sm);
             } else {
-                stream<D, true, true, true>(w, v_prev, k_next, p_prev, s_cur, s_next, p_cur, sm);
+                stream<D, true, true, true, false, true>(w, v_prev, k_next, v_cur, bar, ring, p_prev, s_cur, s_next,
+                                                         p_cur, sm);
                 finish_softmax();
             }
             if (t + 1 < nkt) mask(s_next, next_valid());
@@ -738,32 +775,33 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // Iterations run in pairs (t, t+1), t odd, with one barrier per pair: waves may drift apart
         // within a pair.  A pair reads K_{t+1}, K_{t+2}, V_{t-1}, V_t; at its start the loading
         // waves issue the next pair's tiles K_{t+3}, K_{t+4}, V_{t+1}, V_{t+2}, into the buffers of
-        // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; at its end
-        // they wait for those loads, and the barrier publishes them.
+        // K_{t-1}, K_t, V_{t-3}, V_{t-2}, all last read before the previous barrier; near its end
+        // (before the last kPrefetch slots of its last stream, whose operands are in registers
+        // by then) they wait for those loads, and the barrier publishes them, so that the slots
+        // after it may read the next pair's first operands.
         static_assert(C::NSTAGE == 4, "two pairs of iterations cycle through the four buffers");
         auto pair = [&](auto ph0, auto ph1, int t) __attribute__((always_inline)) {
             load_k(t + 3);
             load_k(t + 4);
             load_v(t + 1);
             load_v(t + 2);
-            body(ph0, t, pp, pp, sB, sA);  // odd t: S_t in sB
-            if (t + 1 < nkt) body(ph1, t + 1, pp, pp, sA, sB);
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-            __syncthreads();
+            body(ph0, t, pp, pp, sB, sA, t + 1 >= nkt);  // odd t: S_t in sB
+            if (t + 1 < nkt) body(ph1, t + 1, pp, pp, sA, sB, true);
         };
         using Ph0 = std::integral_constant<int, 0>;
         using Ph1 = std::integral_constant<int, 1>;
         using Ph2 = std::integral_constant<int, 2>;
         using Ph3 = std::integral_constant<int, 3>;
-        body(Ph0{}, 0, pp, pp, sA, sB);  // scores S_1 -> sB
-        __syncthreads();                 // K_1's buffer is refilled by the first pair
+        // scores S_1 -> sB; then (in the stream) a barrier: K_1's buffer is refilled by the first
+        // pair
+        body(Ph0{}, 0, pp, pp, sA, sB, true);
         // pairs (t, t+1) and (t+2, t+3); the last iterations may end a pair early
         for (int t = 1; t < nkt; t += 4) {
             pair(Ph1{}, Ph2{}, t);
             if (t + 2 < nkt) pair(Ph3{}, Ph0{}, t + 2);
         }
         // P.V of the last tile
-        stream<D, true, false, false>(w, vbuf(nkt - 1), kbuf(0), pp, sA, sA, pp, sm);
+        stream<D, true, false, false, false, false>(w, vbuf(nkt - 1), kbuf(0), 0, false, ring, pp, sA, sA, pp, sm);
 
         // ---- epilogue: normalise, LSE, fold in the running result if there is one, store (the
         // final output; or, for a stream-K segment, an fp32 partial and its LSE in the segment's
