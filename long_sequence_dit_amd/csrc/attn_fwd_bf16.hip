@@ -301,8 +301,7 @@ __host__ __device__ constexpr int last_a_slot() {
 struct Soft {
     float mt[11];           // partial maxima
     float m0, m1;           // row max of each half of the wave
-    float m_new, alpha;     // the tile's reference; 2^(old reference - m_new) when moved
-    bool moved;             // some row's reference moved (wave-uniform)
+    float m_new, alpha;
     float x[16][2];         // stage A results (scaled, shifted scores)
     float e[16][2];         // stage B results (probabilities)
 };
@@ -381,18 +380,10 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
         // after a move), O and l share the reference (consistent), and LSE = r + log2 l.  A NaN
         // row max (a NaN score) moves the reference to NaN, which makes the rescale factor and
         // so the row's output and LSE NaN.  Lanes l and l+32 hold the same row and agree.
-        // Most tiles move no row's reference: one wave-wide test then skips the rest (the new
-        // reference, the factor 2^(r - r_new) and the rescale after the stream).
         const float m_tile = vmax(sm.m0, sm.m1) * w.c;  // max(m0, m1)
-        sm.moved = __builtin_amdgcn_ballot_w64(!(m_tile <= w.m_run)) != 0;
-        if (sm.moved) {
-            asm volatile("");  // a branch, not selects computed on every tile
-            sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
-            sm.alpha = fast_exp2(w.m_run - sm.m_new);
-            w.m_run = sm.m_new;
-        } else {
-            sm.m_new = w.m_run;
-        }
+        sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
+        sm.alpha = fast_exp2(w.m_run - sm.m_new);
+        w.m_run = sm.m_new;
     }
     pair_stages<POS, last_a_slot<D>()>(w.c, sm, s, p);
 }
@@ -730,7 +721,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // after the softmax of a tile: the rare rescale of the running output and row sums (the
         // latter with the factor of the query whose sum the lane_it holds)
         auto finish_softmax = [&]() {
-            if (sm.moved) {
+            if (__builtin_amdgcn_ballot_w64(sm.alpha != 1.f)) {
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
