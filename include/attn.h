@@ -142,11 +142,14 @@ attn_status_t attn_lse_merge(int32_t n, const float* const* o_parts, const float
  * results [B,H,Sq,D] plus their LSE [B,H,Sq] (each part 256-byte aligned):
  * n of them for ATTN_MERGE_NWAY, one (the running result) for
  * ATTN_MERGE_ONLINE, none for ATTN_MERGE_FUSED or when n_chunks == 1.  Then,
- * for a shape whose query tiles of 256 rows leave the last round of the
- * current device's CUs part-full, room for the balanced tail (see
- * attn_shard_fwd): 2 * CUs * 256 * (D + 1) fp32 values (nothing when the
- * tiles fill whole rounds).  The slots are required; the tail's room is
- * optional (without it, whole query tiles throughout).
+ * for a shape of more than one round of query tiles (256 rows each) on the
+ * current device's CUs, 4 KiB of work-queue counters (see attn_shard_fwd);
+ * then, for a shape whose query tiles leave the last round part-full, room
+ * for the balanced tail: (R * CUs + n_tail) slots of 256 * (D + 1) fp32
+ * values, n_tail the query tiles of the last round, R = 4 when there is
+ * more than one round, else 1 (nothing when the tiles fill whole rounds).
+ * The slots are required; the room after them is optional (without it,
+ * whole query tiles throughout, one workgroup each).
  * Returns 0 as well for invalid arguments; attn_shard_fwd reports those.
  */
 size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, int32_t n_chunks, uint32_t flags);
@@ -172,6 +175,13 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *              equal run of (query tile, key tile) pairs, and a second kernel
  *              merges the runs' fp32 partials by their LSE (the balanced tail;
  *              only with the workspace: none given, whole tiles throughout).
+ *              A bf16 launch of several rounds of query tiles and at least
+ *              512 key tiles of work per CU runs persistent: one workgroup
+ *              per CU takes whole query tiles, then the tail's runs (up to
+ *              4 per CU, each at least 64 key tiles), from per-XCD work
+ *              queues in the workspace, so that the XCDs end together
+ *              whatever their clocks.  Which workgroup takes an item does
+ *              not change the result.
  *              ONLINE and NWAY run one kernel per chunk
  *              (each with the balanced tail when it pays).  ONLINE is the
  *              ring's step: each chunk's kernel folds its result into the
@@ -212,9 +222,12 @@ attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, at
  * contents (nothing in it needs to start at zero): calls that overlap on one
  * device (two streams, or two threads) race on it and must be serialised by
  * the caller.  Arguments, results and errors are those of attn_shard_fwd with
- * flags = ATTN_MERGE_FUSED; the result is bitwise that of attn_shard_fwd with
- * a workspace of attn_shard_workspace_size() bytes on a device of at most 256
- * CUs.
+ * flags = ATTN_MERGE_FUSED.  It launches one workgroup per item with at most
+ * one tail run per CU (never persistent), so on a device of at most 256 CUs
+ * its result is bitwise that of attn_shard_fwd with a workspace of
+ * attn_shard_workspace_size() bytes for the launches attn_shard_fwd does not
+ * run persistent; for the others attn_shard_fwd may cut the tail into more
+ * runs, and the two agree to fp32 rounding.
  */
 #define ATTN_NOALLOC_SCRATCH_BYTES 67633152u
 attn_status_t attn_shard_fwd_noalloc(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks,

@@ -96,6 +96,23 @@ int debug_wg_order() {
     return 0;
 }
 
+// Debug aids for tests: LSDIT_DEBUG_PERSIST=0 never runs the bf16 kernel persistent, =1 does so
+// for every launch of more than one round (whatever its work per CU); LSDIT_DEBUG_TAIL_RUNS=k
+// (1..kSkMaxRunsPerCu) fixes a persistent launch's tail runs per CU.  -1: not set.
+int debug_persist() {
+    const char* e = getenv("LSDIT_DEBUG_PERSIST");
+    if (!e) return -1;
+    if (strcmp(e, "0") == 0) return 0;
+    if (strcmp(e, "1") == 0) return 1;
+    return -1;
+}
+int debug_tail_runs() {
+    const char* e = getenv("LSDIT_DEBUG_TAIL_RUNS");
+    if (!e) return -1;
+    const int k = atoi(e);
+    return k >= 1 && k <= 4 ? k : -1;
+}
+
 int device_cus() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -111,28 +128,57 @@ int device_cus() {
 // as 20-30 key tiles (bf16: at 22 tiles, the 4,608-token image shape ran 4.5% slower with the
 // tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).  The FP8
 // kernel's tiles take half the time, so its fixed costs weigh about twice as many tiles.
+//
+// A launch of several rounds runs the bf16 kernel persistent (FwdArgs::persist): one workgroup
+// per CU taking items from per-XCD work queues, so that the fast XCDs take over the slow ones'
+// remaining work (the XCDs' clocks differ by up to ~8%, and a static grid ends with the slowest
+// XCD).  Its tail is then cut into up to kSkMaxRunsPerCu runs per CU, each at least
+// kSkMinRunTiles key tiles long, so that the end balances to a fraction of a query tile; the
+// queues' extra cost (a few microseconds per item) pays off from about kPersistMinTiles key
+// tiles per CU (44,160-key shares: 4-7% faster on the slowest boxes seen, 0.5-1% on the
+// fastest; the 4,608-token image shape, 121 tiles per CU, ran 3-10% slower persistent).
 struct SkPlan {
     int n_dp = 0;    // query tiles run whole
-    int sk_wgs = 0;  // workgroups of the tail (0 = no tail)
+    int sk_wgs = 0;  // runs of the tail (0 = no tail)
 };
 constexpr int64_t kSkMinSavingBf16 = 40;
 constexpr int64_t kSkMinSavingFp8 = 64;
+constexpr int kSkMaxRunsPerCu = 4;
+constexpr int64_t kSkMinRunTiles = 64;
+constexpr int64_t kPersistMinTiles = 512;
 
-SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving) {
+// runs_per_cu: the most runs per CU (1 for a launch of one workgroup per item)
+SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int runs_per_cu = 1) {
     SkPlan p;
     if (n_q <= 0 || T <= 0 || cus <= 0 || n_q > 0x7FFFFFFF) return p;
     const int64_t rem = n_q % cus;
     if (rem == 0 || T * (cus - rem) / cus < min_saving) return p;
     const int64_t U = rem * T;  // > rem, since T > min_saving >= 1: every run is at most T long
+    int64_t k = U / ((int64_t)cus * kSkMinRunTiles);
+    k = k < 1 ? 1 : (k > runs_per_cu ? runs_per_cu : k);
+    const int dk = debug_tail_runs();
+    if (runs_per_cu > 1 && dk > 0) k = dk;
     p.n_dp = (int)(n_q - rem);
-    p.sk_wgs = (int)(U < cus ? U : cus);
+    p.sk_wgs = (int)(U < cus * k ? U : cus * k);
     return p;
 }
 
-// Query tiles of the bf16 kernel, and the workspace of its tail: 2 slots per workgroup.
+// Query tiles of the bf16 kernel, and the workspace of its tail: one partial slot per run and
+// one per tail tile boundary (lsdit::sk_slot), each of kSkRows rows of D fp32 values and an LSE.
 int64_t n_qtiles(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows); }
-size_t sk_o_bytes(int sk_wgs, int D) { return align_up((size_t)2 * sk_wgs * lsdit::kSkRows * D * 4); }
-size_t sk_bytes(int sk_wgs, int D) { return sk_o_bytes(sk_wgs, D) + align_up((size_t)2 * sk_wgs * lsdit::kSkRows * 4); }
+int64_t sk_slots(const SkPlan& p, int64_t n_q) { return p.sk_wgs ? p.sk_wgs + (n_q - p.n_dp) : 0; }
+size_t sk_o_bytes(int64_t n_slots, int D) { return align_up((size_t)n_slots * lsdit::kSkRows * D * 4); }
+size_t sk_bytes(int64_t n_slots, int D) { return sk_o_bytes(n_slots, D) + align_up((size_t)n_slots * lsdit::kSkRows * 4); }
+// The work queues of a persistent launch, in the workspace before the tail's partials: present
+// when the query tiles take more than one round.
+constexpr size_t kWqBytes = (size_t)lsdit::kWorkQueueWords * 4;
+size_t wq_bytes(int64_t n_q, int cus) { return n_q > cus ? kWqBytes : 0; }
+// The most room a shape's tail can take: runs of up to kSkMaxRunsPerCu per CU when persistent
+size_t tail_room(int64_t n_q, int cus, int D) {
+    const int64_t rem = n_q % cus;
+    if (rem == 0) return 0;
+    return sk_bytes((n_q > cus ? kSkMaxRunsPerCu : 1) * (int64_t)cus + rem, D);
+}
 
 // The FP8 call's workspace: V^T tiles, then the balanced tail's partials when it runs.
 size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
@@ -154,7 +200,8 @@ int slots_for(uint32_t flags, int32_t n) {
 
 
 // ---- the static scratch of attn_shard_fwd_noalloc: the balanced tail's partials (fp32 O, then
-// fp32 LSE, as in a workspace) of at most kScratchTailWgs workgroups at D <= 128.
+// fp32 LSE, as in a workspace) of at most kScratchTailWgs runs at D <= 128 (launches one
+// workgroup per item, at most one run per CU: fewer than 2 * kScratchTailWgs slots).
 constexpr int kScratchTailWgs = 256;
 constexpr size_t kScratchBytes = ((size_t)2 * kScratchTailWgs * lsdit::kSkRows * 128 * 4 + kAlign - 1) / kAlign * kAlign +
                                  ((size_t)2 * kScratchTailWgs * lsdit::kSkRows * 4 + kAlign - 1) / kAlign * kAlign;
@@ -243,11 +290,18 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
         if (!workspace || ws_bytes < slots_need) return ATTN_ERR_WORKSPACE;
         if (!ws_aligned) return ATTN_ERR_ALIGN;
     }
+    // after the chunk slots: the work queues (shapes of more than one round), then the tail
+    const int64_t n_q = n_qtiles(B, H, Sq);
+    const int cus = device_cus();
+    const size_t wq_need = wq_bytes(n_q, cus);
+    unsigned* wq = nullptr;
     void* tail_ws = nullptr;
     size_t tail_bytes = 0;
-    if (!scratch && workspace && ws_aligned && ws_bytes > slots_need) {
-        tail_ws = (char*)workspace + slots_need;
-        tail_bytes = ws_bytes - slots_need;
+    if (!scratch && workspace && ws_aligned && ws_bytes >= slots_need + wq_need) {
+        if (wq_need) wq = (unsigned*)((char*)workspace + slots_need);
+        tail_ws = (char*)workspace + slots_need + wq_need;
+        tail_bytes = ws_bytes - slots_need - wq_need;
+        if (tail_bytes == 0) tail_ws = nullptr;
     }
 
     const hipStream_t s = (hipStream_t)stream;
@@ -274,28 +328,36 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
         a.o = slot_o(i); a.os = cs; a.o_bf16 = 0; a.lse = slot_lse(i);
     };
     auto ok = [](hipError_t e) { return e == hipSuccess; };
-    const int64_t n_q = n_qtiles(B, H, Sq);
-    const int cus = device_cus();
     const int tail_cus = scratch && cus > kScratchTailWgs ? kScratchTailWgs : cus;
 
     // One kernel launch over a's chunk list (T key tiles) into a's output, folding in a's running
-    // result if it has one.  When its query tiles leave the last round of CUs part-full, that
-    // round's work is spread evenly (the balanced tail) as far as the tail's room allows, and the
-    // fix-up kernel merges the runs' partials (and the running result) into the output.
+    // result if it has one.  A bf16 launch of several rounds with enough work per CU runs
+    // persistent when the workspace holds the work queues.  When the query tiles leave the last
+    // round of CUs part-full, that round's work is spread evenly (the balanced tail) as far as the
+    // tail's room allows, and the fix-up kernel merges the runs' partials (and the running result)
+    // into the output.
     auto launch = [&](FwdArgs a, int64_t T) -> attn_status_t {
-        const SkPlan p = in_dt == ATTN_BF16 ? sk_plan(n_q, T, tail_cus, kSkMinSavingBf16) : SkPlan{};
+        const bool bf16 = in_dt == ATTN_BF16;
+        bool persist = bf16 && wq && n_q * T >= kPersistMinTiles * cus;
+        if (debug_persist() >= 0) persist = bf16 && wq && debug_persist() == 1;
+        if (persist) {
+            a.persist = cus;
+            a.wq = wq;
+        }
+        const SkPlan p = bf16 ? sk_plan(n_q, T, tail_cus, kSkMinSavingBf16, persist ? kSkMaxRunsPerCu : 1) : SkPlan{};
+        const int64_t n_slots = sk_slots(p, n_q);
         void* tw = tail_ws;
         size_t tb = tail_bytes;
         if (scratch && p.sk_wgs) {
-            if (sk_bytes(p.sk_wgs, D) > kScratchBytes) return ATTN_ERR_WORKSPACE;  // not with D <= 128
+            if (sk_bytes(n_slots, D) > kScratchBytes) return ATTN_ERR_WORKSPACE;  // not with D <= 128
             if (!ok(scratch_address(&tw))) return ATTN_ERR_HIP;
             tb = kScratchBytes;
         }
-        if (p.sk_wgs == 0 || !tw || tb < sk_bytes(p.sk_wgs, D)) return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
+        if (p.sk_wgs == 0 || !tw || tb < sk_bytes(n_slots, D)) return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
         a.sk_o = (float*)tw;
-        a.sk_lse = (float*)((char*)tw + sk_o_bytes(p.sk_wgs, D));
+        a.sk_lse = (float*)((char*)tw + sk_o_bytes(n_slots, D));
         if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
         lsdit::SkFixupArgs f{};
         f.B = B; f.H = H; f.Sq = Sq; f.D = D;
@@ -419,11 +481,12 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
     if (B < 0 || H < 0 || Sq < 0 || (D != 64 && D != 128) || n_chunks < 1 || n_chunks > ATTN_MAX_CHUNKS) return 0;
     const int slots = slots_for(flags, n_chunks);
     if (slots < 0) return 0;
-    // the chunk slots, then room for the balanced tail of shapes whose query tiles leave the last
-    // round part-full (whether it runs also depends on the key count)
+    // the chunk slots, then the work queues of shapes of more than one round, then room for the
+    // balanced tail of shapes whose query tiles leave the last round part-full (whether the
+    // queues and the tail are used also depends on the key count)
     const int cus = device_cus();
     const int64_t n_q = n_qtiles(B, H, Sq);
-    return (size_t)slots * slot_bytes(B, H, Sq, D) + (n_q % cus != 0 ? sk_bytes(cus, D) : 0);
+    return (size_t)slots * slot_bytes(B, H, Sq, D) + wq_bytes(n_q, cus) + tail_room(n_q, cus, D);
 }
 
 attn_status_t attn_shard_fwd(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
@@ -475,7 +538,7 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
 size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t Skv, int32_t D) {
     if (B <= 0 || H <= 0 || Sq < 0 || Skv <= 0 || D != 128) return 0;
     const SkPlan p = fp8_plan(B, H, Sq, Skv);
-    return fp8_vt_bytes(B, H, Skv) + (p.sk_wgs ? sk_bytes(p.sk_wgs, D) : 0);
+    return fp8_vt_bytes(B, H, Skv) + (p.sk_wgs ? sk_bytes(sk_slots(p, n_qtiles(B, H, Sq)), D) : 0);
 }
 
 attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
@@ -521,7 +584,7 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
         a.sk_o = (float*)((char*)workspace + fp8_vt_bytes(B, H, Skv));
-        a.sk_lse = (float*)((char*)a.sk_o + sk_o_bytes(p.sk_wgs, D));
+        a.sk_lse = (float*)((char*)a.sk_o + sk_o_bytes(sk_slots(p, n_qtiles(B, H, Sq)), D));
     }
     if (lsdit::launch_fp8_pack_v(a, s) != hipSuccess) return ATTN_ERR_HIP;
     if (lsdit::launch_fwd_fp8(a, s) != hipSuccess) return ATTN_ERR_HIP;

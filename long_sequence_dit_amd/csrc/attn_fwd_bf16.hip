@@ -51,6 +51,10 @@
 // Workgroups are remapped so that each XCD (workgroups are dealt to the 8
 // XCDs round-robin) runs consecutive query tiles of the same head, which
 // then share K/V tiles in that XCD's L2.
+// Long launches run persistent: one workgroup per CU, taking items (whole
+// query tiles, then the tail's runs) from per-XCD work queues, so that the
+// XCDs, whose clocks differ by several percent, end together: a fast XCD
+// takes a slow one's remaining whole tiles first, then runs from any queue.
 #include "kernels.h"
 
 #include <atomic>
@@ -97,7 +101,8 @@ struct Cfg {
     static constexpr int TILE_BYTES = BK * ROW_BYTES;
     static constexpr int NSTAGE = 4;                        // LDS buffers per tensor (loop unrolled by NSTAGE)
     static constexpr int V_REGION = NSTAGE * TILE_BYTES;    // K buffers below, V buffers from here
-    static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;
+    static constexpr int ITEM_ADDR = 2 * NSTAGE * TILE_BYTES;  // the next item, broadcast to the waves
+    static constexpr int LDS_BYTES = ITEM_ADDR + 16;
     static constexpr int ROWS_PER_BLK = 64 / CH;            // rows one wave-wide 1 KiB load covers
     static constexpr int BLKS = BK / ROWS_PER_BLK;          // 1 KiB blocks per tile
     // Waves 0-3 (one per SIMD) issue all tile loads.  Each SIMD runs wave w and wave w+4,
@@ -124,6 +129,35 @@ __device__ __forceinline__ int v_swz(int row) {
     const int s0 = row & 1, s1 = (row >> 1) & 1;
     if constexpr (D == 128) return 10 * s0 + 4 * s1;
     else return 2 * s0 + 4 * s1;
+}
+
+// The next item of a persistent workgroup on XCD xcd (FwdArgs: a grid of G workgroups took
+// items 0 .. G-1 first).  The remaining items are split by b % 8 == x, the XCD a round-robin
+// dispatch would give them (so xcd_remap's locality holds), over 8 queues of whole query tiles
+// (counter x: items G <= b < n_whole) and 8 queues of tail runs (counter 8 + x: items
+// max(G, n_whole) <= b < n_items), each handed out in increasing order.  The workgroup takes
+// from its own XCD's whole-tile queue, then from the others' (the longest items go first), then
+// from the tail queues in the same order; -1 when all are empty.  A queue found empty is marked
+// in `empty` and not asked again.  Relaxed atomics: an item only needs a unique index, and
+// items write disjoint outputs.
+__device__ __forceinline__ int wq_next(unsigned* wq, int xcd, int G, int n_whole, int n_items, unsigned& empty) {
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+        const int x = (xcd + k) & 7, qi = (k & 8) | x;
+        const int lo = k < 8 ? G : (G > n_whole ? G : n_whole), hi = k < 8 ? n_whole : n_items;
+        const int first = lo + ((x - lo) & 7);  // the queue's first item
+        if ((empty >> qi) & 1u) continue;
+        if (first < hi) {
+            const int b = first + 8 * (int)atomicAdd(wq + qi * kWorkQueueStride, 1u);
+            if (b < hi) return b;
+        }
+        empty |= 1u << qi;
+    }
+    return -1;
+}
+
+__global__ void wq_clear_kernel(unsigned* wq) {
+    if (threadIdx.x < kWorkQueueWords / kWorkQueueStride) wq[threadIdx.x * kWorkQueueStride] = 0u;
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin; give XCD x a contiguous
@@ -530,29 +564,52 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
     int nkt_all = 0;  // tiles over all chunks
     for (int ci = 0; ci < n_chunks; ++ci) nkt_all += (__builtin_amdgcn_readlane(v_len, ci) + C::BK - 1) / C::BK;
 
-    // ---- this workgroup's work: segments (query tile, run of the key-tile sequence).
-    // Without a stream-K tail the grid is the B*H*n_qt query tiles, one whole tile each.  With
-    // one, workgroups below n_dp take whole query tiles (remapped over that part alone) and the
-    // others, which follow them in dispatch order, an equal run of the tail's units, which spans
-    // at most two query tiles.
-    // Only seg is carried from one segment to the next: each iteration derives its segment from
-    // the workgroup index again (state kept live across the key loop would cost registers).
-    for (int seg = 0;; ++seg) {
+    // ---- this workgroup's work: items (FwdArgs), each one or two segments (query tile, run of
+    // the key-tile sequence).  A whole query tile is one segment; a tail run spans at most two
+    // query tiles.  The first item is the workgroup's own index; a persistent workgroup then
+    // takes items from the work queues (wq_next) until they are empty.
+    // Only the item and seg are carried from one segment to the next: each iteration derives its
+    // segment from them again (state kept live across the key loop would cost registers).
+    int seg = 0, bid = 0;
+    unsigned wq_empty = 0;  // queues found empty (thread 0's)
+    for (int it = 0;; ++it) {
         // the arguments, read through a pointer the compiler cannot follow: so their loads stay
         // in the iteration rather than being hoisted in front of the loop and held in registers
         // across it
         const kernarg_t<FwdArgs>* ap = (const kernarg_t<FwdArgs>*)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
         const kernarg_t<FwdArgs>& ar = *ap;
-        const int bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
+        const int n_whole = ar.sk_wgs == 0 ? n_qtiles : ar.n_dp;
+        if (seg == 0) {
+            if (it == 0) {
+                bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
+            } else {
+                if (ar.persist == 0) break;
+                // every wave is done with the last item's tiles (and no load is in flight) before
+                // the next item's prologue rewrites LDS, and has read the last broadcast
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                __syncthreads();
+                if (tid == 0) {
+                    const int xcd = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // XCC_ID[3:0]
+                    *(int*)(smem + C::ITEM_ADDR) =
+                        wq_next(ar.wq, xcd, (int)gridDim.x, n_whole, n_whole + ar.sk_wgs, wq_empty);
+                }
+                __syncthreads();
+                bid = __builtin_amdgcn_readfirstlane(*(volatile int*)(smem + C::ITEM_ADDR));
+                if (bid < 0) break;
+            }
+        }
         // likewise the lane index: values derived from it are computed in the iteration
         int lane_it = lane;
         asm volatile("" : "+v"(lane_it));
         const int hi_it = lane_it >> 5;
-        int sk_w = -1, tile, g_first, nkt;
-        if (ar.sk_wgs == 0 || bid < ar.n_dp) {
-            if (seg > 0) break;
-            tile = xcd_remap(bid, ar.sk_wgs == 0 ? n_qtiles : ar.n_dp);
+        int sk_slot_ = -1, tile, g_first, nkt;
+        if (bid < n_whole) {
+            if (seg > 0) {
+                seg = 0;
+                continue;
+            }
+            tile = xcd_remap(bid, n_whole);
             g_first = 0;
             nkt = nkt_all;
         } else {
@@ -561,13 +618,17 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             // whole number of query tiles (the ring share) or half of one (the full
             // sequence): they stream the same key tiles together and share them in the L2
             // (remapped to consecutive runs, their starts spread over the whole key range)
-            sk_w = bid - ar.n_dp;
+            const int sk_w = bid - ar.n_dp;
             const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1
             const int64_t cut = (u0 / nkt_all + 1) * nkt_all;
             const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
-            if (seg > 1 || s0 >= s1) break;
+            if (seg > 1 || s0 >= s1) {
+                seg = 0;
+                continue;
+            }
+            sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / nkt_all), ar.sk_wgs);
             tile = ar.n_dp + (int)(s0 / nkt_all);
             g_first = (int)(s0 % nkt_all);
             nkt = (int)(s1 - s0);
@@ -577,13 +638,14 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         tile = __builtin_amdgcn_readfirstlane(tile);
         g_first = __builtin_amdgcn_readfirstlane(g_first);
         nkt = __builtin_amdgcn_readfirstlane(nkt);
-        sk_w = __builtin_amdgcn_readfirstlane(sk_w);
+        sk_slot_ = __builtin_amdgcn_readfirstlane(sk_slot_);
         if (seg > 0) {
             // every wave is done with the previous segment's tiles (and no load is in flight)
             // before this segment's prologue rewrites LDS
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             __syncthreads();
         }
+        ++seg;
         const int bh = tile / n_qt, qt = tile % n_qt;
         const int b = bh / ar.H, h = bh % ar.H;
         const unsigned short* qp = (const unsigned short*)ar.q + b * ar.qs.b + h * ar.qs.h;
@@ -804,7 +866,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             // output element o = wc * acc + wr * O_run (wc = 1/l without a running result)
             float lse_out = lse2 * kLn2, wc = inv_l, wr = 0.f;
             const float* rp = nullptr;
-            if (sk_w < 0 && ar.run_lse) {
+            if (sk_slot_ < 0 && ar.run_lse) {
                 const int64_t rrow = (int64_t)bh * ar.Sq + qrow;
                 rp = ar.run_o + rrow * D + 4 * hi_it;
                 lse_out = fold_weights(lse_out, ar.run_lse[rrow], wc, wr);
@@ -818,7 +880,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                 if (rp) x += wr * *(const f32x4_t*)(rp + 32 * dt + 8 * r4);
                 return x;
             };
-            if (sk_w < 0 && ar.o_bf16) {
+            if (sk_slot_ < 0 && ar.o_bf16) {
                 unsigned short* op = (unsigned short*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
@@ -835,11 +897,11 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             } else {
                 float* op;
                 float* lp;
-                if (sk_w < 0) {
+                if (sk_slot_ < 0) {
                     op = (float*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
                     lp = ar.lse + (int64_t)bh * ar.Sq + qrow;
                 } else {
-                    const int64_t r = (int64_t)(2 * sk_w + seg) * kSkRows + (qrow - qt * C::BQ);
+                    const int64_t r = (int64_t)sk_slot_ * kSkRows + (qrow - qt * C::BQ);
                     op = ar.sk_o + r * D;
                     lp = ar.sk_lse + r;
                 }
@@ -877,9 +939,18 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
             return hipErrorInvalidValue;
         n_tiles = (int64_t)a.n_dp + a.sk_wgs;
     }
-    if (n_tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (n_tiles > 0x7FFFFFFF || a.persist < 0 || (a.persist > 0 && !a.wq)) return hipErrorInvalidValue;
     const float c = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)n_tiles), dim3(C::NT), C::LDS_BYTES, stream, a, n_qt, c);
+    FwdArgs ka = a;
+    int64_t grid = n_tiles;
+    if (a.persist > 0 && n_tiles > a.persist) {
+        // the queues start empty (a kernel, not a memset, so that the launch can be captured)
+        hipLaunchKernelGGL(wq_clear_kernel, dim3(1), dim3(64), 0, stream, a.wq);
+        grid = a.persist;
+    } else {
+        ka.persist = 0;  // one round: every item has its own workgroup
+    }
+    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(C::NT), C::LDS_BYTES, stream, ka, n_qt, c);
     return hipGetLastError();
 }
 

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         int lane = tid & 63;
         asm volatile("" : "+v"(lane));
         const int hi = lane >> 5;
-        int sk_w = -1, gidx, g_first, nkt;
+        int sk_slot_ = -1, gidx, g_first, nkt;
         if (ar.sk_wgs == 0 || bid < ar.n_dp) {
             if (seg > 0) break;
             gidx = xcd_remap(bid, ar.sk_wgs == 0 ? n_q : ar.n_dp);
@@ -440,12 +440,13 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             // whole number of query tiles (the ring share) or half of one (the full
             // sequence): they stream the same key tiles together and share them in the L2
             // (remapped to consecutive runs, their starts spread over the whole key range)
-            sk_w = bid - ar.n_dp;
+            const int sk_w = bid - ar.n_dp;
             const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             const int64_t cut = (u0 / n_kt + 1) * n_kt;
             const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
             if (seg > 1 || s0 >= s1) break;
+            sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / n_kt), ar.sk_wgs);
             gidx = ar.n_dp + (int)(s0 / n_kt);
             g_first = (int)(s0 % n_kt);
             nkt = (int)(s1 - s0);
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         gidx = __builtin_amdgcn_readfirstlane(gidx);
         g_first = __builtin_amdgcn_readfirstlane(g_first);
         nkt = __builtin_amdgcn_readfirstlane(nkt);
-        sk_w = __builtin_amdgcn_readfirstlane(sk_w);
+        sk_slot_ = __builtin_amdgcn_readfirstlane(sk_slot_);
         if (seg > 0) {
             // every wave is done with the previous segment's tiles (and no load is in flight)
             // before this segment's prologue rewrites LDS
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
         const float inv_l = ar.v_descale / l_tot;
         const float lse2 = w.m_run + log2f(l_tot) - kPShift;
         if (qrow < ar.Sq) {
-            if (sk_w < 0 && ar.o_bf16) {
+            if (sk_slot_ < 0 && ar.o_bf16) {
                 unsigned short* op = (unsigned short*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
 #pragma unroll
                 for (int dt = 0; dt < D / 32; ++dt)
@@ -660,11 +661,11 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
                 // the final fp32 output, or a tail segment's fp32 partial and LSE in its slot
                 float* op;
                 float* lp;
-                if (sk_w < 0) {
+                if (sk_slot_ < 0) {
                     op = (float*)ar.o + b * ar.os.b + h * ar.os.h + (int64_t)qrow * ar.os.s;
                     lp = ar.lse + (int64_t)bh * ar.Sq + qrow;
                 } else {
-                    const int64_t r = (int64_t)(2 * sk_w + seg) * kSkRows + (qrow - qt * BQ);
+                    const int64_t r = (int64_t)sk_slot_ * kSkRows + (qrow - qt * BQ);
                     op = ar.sk_o + r * D;
                     lp = ar.sk_lse + r;
                 }

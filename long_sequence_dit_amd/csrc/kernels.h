@@ -32,21 +32,28 @@ struct FwdArgs {
     int n_chunks;        // 1 .. kMaxChunks
     int chunk_row[kMaxChunks];
     int chunk_len[kMaxChunks];  // each > 0
-    // Balanced tail (bf16 path): sk_wgs > 0 launches n_dp + sk_wgs
-    // workgroups.  Workgroups below n_dp take one whole query tile each (query tiles
-    // 0 .. n_dp-1 of the n_q = B*H*ceil(Sq/kSkRows) in (b, h, tile) order) and write the final
-    // output.  The other query tiles make U = (n_q - n_dp) * T units (query tile, key tile), T
-    // key tiles per query tile; stream-K workgroup w takes units [sk_start(U, w, sk_wgs),
+    // The launch's work is a list of items, logical indices b < n_items.  Without a balanced tail
+    // (sk_wgs == 0) item b is query tile xcd_remap(b, n_q) of the n_q = B*H*ceil(Sq/kSkRows) in
+    // (b, h, tile) order, taken whole; n_items = n_q.
+    // Balanced tail (bf16 and FP8 paths): sk_wgs > 0 makes n_items = n_dp + sk_wgs.  Items below
+    // n_dp are whole query tiles (xcd_remap over the first n_dp) and write the final output.  The
+    // other query tiles make U = (n_q - n_dp) * T units (query tile, key tile), T key tiles per
+    // query tile; item n_dp + w is the tail's run w, units [sk_start(U, w, sk_wgs),
     // sk_start(U, w + 1, sk_wgs)): at most two query-tile segments, because sk_wgs > n_q - n_dp
-    // makes every range at most T long.  With sk_wgs == 0 the grid is one workgroup per query
-    // tile.  Segment i of workgroup w is written as an fp32 partial
-    // (normalised by its own row sum) with its natural-log LSE into slot 2w + i: row r of the
-    // query tile at sk_o + slot*kSkRows*D + r*D and sk_lse + slot*kSkRows + r.
-    // launch_sk_fixup then merges the partials into the final output.
+    // makes every run at most T long.  Each segment is written as an fp32 partial (normalised by
+    // its own row sum) with its natural-log LSE into slot sk_slot(...): row r of the query tile
+    // at sk_o + slot*kSkRows*D + r*D and sk_lse + slot*kSkRows + r.  launch_sk_fixup then merges
+    // the partials into the final output.
     int n_dp;
-    int sk_wgs;          // 0 = no stream-K tail
+    int sk_wgs;          // runs of the tail; 0 = no tail
     float* sk_o;
     float* sk_lse;
+    // Dispatch (bf16 path).  persist == 0: one workgroup per item.  persist > 0: a persistent
+    // grid of min(n_items, persist) workgroups (one per CU); workgroup g takes item g, then
+    // further items from the work queues in wq (kWorkQueueWords words, zeroed before the
+    // launch), until they are empty.  Results do not depend on which workgroup takes an item.
+    int persist;
+    unsigned* wq;
     // Running result over earlier keys (the ring's online merge done in the epilogue): when
     // run_lse is set, the output written is the LSE merge (fold_weights) of this launch's result
     // with run_o [B, H, Sq, D] fp32 contiguous / run_lse [B, H, Sq].  o and lse may alias them
@@ -86,9 +93,20 @@ __device__ __forceinline__ float fold_weights(float lse_c, float lse_r, float& w
     return m + logf(s);
 }
 
-// Query rows per query tile of the bf16 kernel, and the first unit of stream-K workgroup w.
+// Query rows per query tile of the bf16 kernel, and the first unit of stream-K run w.
 constexpr int kSkRows = 256;
 __host__ __device__ inline int64_t sk_start(int64_t U, int w, int n_wgs) { return U * w / n_wgs; }
+
+// Partial slot of a tail segment.  A run's first segment (seg 0) takes slot w; a second segment
+// (seg 1) starts at the first unit of tail tile j >= 1, continuing the run from tile j - 1, and
+// takes slot n_runs + j - 1.  Runs are at most T units long, so at most one run crosses each
+// tile boundary: the slots are distinct and number fewer than n_runs + n_tail.
+__host__ __device__ inline int sk_slot(int w, int seg, int j, int n_runs) { return seg == 0 ? w : n_runs + j - 1; }
+
+// The work queues of a persistent launch: 16 counters, each in its own 256-byte line.  Counter
+// x < 8 hands out the whole query tiles of XCD x, counter 8 + x its tail runs.
+constexpr int kWorkQueueStride = 64;
+constexpr int kWorkQueueWords = 16 * kWorkQueueStride;
 
 // Merge of the stream-K partials of query tiles n_dp .. n_q-1 (see FwdArgs).
 struct SkFixupArgs {

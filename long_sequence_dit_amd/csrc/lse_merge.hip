@@ -115,12 +115,13 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     if (d == 0) a.lse[row] = lse_out;
 }
 
-// The stream-K tail of the bf16 kernel (FwdArgs) left, for each query tile j of the tail, fp32
-// partials over consecutive runs of its T key tiles in the slots of the workgroups whose unit
-// ranges meet [jT, (j+1)T).  The first of them is the last workgroup starting at or before jT:
-// w = floor(((jT + 1) P - 1) / U) for P workgroups over U units (ranges may be empty when U < P).
-// A run that starts before jT is its workgroup's second segment.  The runs merge by the LSE rule
-// above; a tile's rows are read and written once.
+// The balanced tail of the forward kernels (FwdArgs) left, for each query tile j of the tail,
+// fp32 partials over consecutive runs of its T key tiles, one per run whose unit range meets
+// [jT, (j+1)T).  The first of them is the last run starting at or before jT:
+// w = floor(((jT + 1) P - 1) / U) for P runs over U units (runs may be empty when U < P).  A run
+// that starts before jT continues into tile j as its second segment (slot P + j - 1, sk_slot);
+// the others start in tile j (slot w).  The runs merge by the LSE rule above; a tile's rows are
+// read and written once.
 __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     const int lanes_per_row = a.D / 4;
     const int rows_per_block = kThreads / lanes_per_row;
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
         const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
         if (u0 >= t1) break;
         if (u1 == u0) continue;
-        const int slot = 2 * w + (u0 < t0 ? 1 : 0);
+        const int slot = sk_slot(w, u0 < t0 ? 1 : 0, j, P);
         const float l = a.sk_lse[(int64_t)slot * kSkRows + r];
         nan |= l != l;
         if (l == -INFINITY || l != l) continue;
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
             const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
             if (u0 >= t1) break;
             if (u1 == u0) continue;
-            const int64_t row = (int64_t)(2 * w + (u0 < t0 ? 1 : 0)) * kSkRows + r;
+            const int64_t row = (int64_t)sk_slot(w, u0 < t0 ? 1 : 0, j, P) * kSkRows + r;
             const f32x4_t x = __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d));
             acc += expf(a.sk_lse[row] - L) * x;
         }

@@ -123,6 +123,18 @@ def _shard(lib, lens=(10, 10), order=None, flags=4, ws=P, ws_bytes=1 << 30, D=12
                               P, None)
 
 
+def _al(n):
+    return -(-n // 256) * 256
+
+
+def _tail_room(n_slots, D=128):
+    """Partial slots of the balanced tail: 256 rows of D fp32 values, then 256 fp32 LSEs, each."""
+    return _al(n_slots * 256 * D * 4) + _al(n_slots * 256 * 4)
+
+
+WQ = 16 * 64 * 4  # the work queues of a persistent launch: 16 counters, 256 bytes apart
+
+
 def test_shard_fwd_argument_errors(attn):
     lib = attn.load()
     assert _shard(lib, lens=()) == SHAPE
@@ -134,7 +146,7 @@ def test_shard_fwd_argument_errors(attn):
     assert _shard(lib, order=(1, -1)) == SHAPE
     assert _shard(lib, flags=0) == UNSUP
     assert _shard(lib, flags=3) == UNSUP
-    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4  # room for the balanced tail (2 x 1 query tiles)
+    tail = _tail_room(256 + 2)  # room for the balanced tail: one run per CU, 2 query tiles
     for flags, n_slots in ((1, 2), (2, 1)):  # n-way and online keep fp32 partials in the workspace
         assert _shard(lib, ws=None, flags=flags) == WS
         need = lib.attn_shard_workspace_size(1, 2, 10, 128, 2, flags)
@@ -152,20 +164,24 @@ def test_workspace_sizes(attn):
     lib = attn.load()
     rows = 1 * 16 * 5520
     slot = -(-rows * 128 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
-    # fused: no chunk partials.  A shape whose query tiles of 256 rows leave the last round of
-    # the GPU's CUs part-full (16 heads x 22 tiles = 352 on 256 CUs; the CPU build assumes 256)
-    # gets room for the balanced tail: 2 slots of 256 rows x (D + 1) fp32 per CU, whatever the
-    # chunking; a shape filling whole rounds (16 x 16 tiles) none.  n-way keeps every chunk's
-    # fp32 partial and online one running result, followed by the same room for the tail (each
-    # chunk's launch may run one).
-    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4
+    # fused: no chunk partials.  A shape of more than one round of query tiles (256 rows each;
+    # the CPU build assumes 256 CUs) gets the work queues of a persistent launch; one whose tiles
+    # leave the last round part-full (16 heads x 22 tiles = 352: 96 in the last round) also room
+    # for the balanced tail: a slot of 256 rows x (D + 1) fp32 per run (up to 4 runs per CU) and
+    # per tail tile, whatever the chunking; a shape filling whole rounds (16 x 16 tiles) none.
+    # n-way keeps every chunk's fp32 partial and online one running result, followed by the same
+    # room (each chunk's launch may use it).
+    tail = WQ + _tail_room(4 * 256 + 96)
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 1) == 8 * slot + tail   # n-way
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 2) == 1 * slot + tail   # online
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 4) == tail
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 1, 4) == tail  # one chunk: same kernel
-    assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == tail  # 2768 tiles: 208 in the last round
+    # 2768 tiles: 208 in the last round
+    assert lib.attn_shard_workspace_size(1, 16, 44160, 128, 8, 4) == WQ + _tail_room(4 * 256 + 208)
     assert lib.attn_shard_workspace_size(1, 16, 4096, 128, 8, 4) == 0
-    assert lib.attn_shard_workspace_size(1, 16, 5520, 64, 8, 4) == 2 * 256 * 256 * 64 * 4 + 2 * 256 * 256 * 4
+    assert lib.attn_shard_workspace_size(1, 32, 4096, 128, 8, 4) == WQ  # two full rounds: queues only
+    assert lib.attn_shard_workspace_size(1, 3, 4096, 128, 8, 4) == _tail_room(256 + 48)  # one round
+    assert lib.attn_shard_workspace_size(1, 16, 5520, 64, 8, 4) == WQ + _tail_room(4 * 256 + 96, 64)
     assert lib.attn_shard_workspace_size(1, 16, 5520, 96, 8, 4) == 0
     assert lib.attn_shard_workspace_size(1, 16, 5520, 128, 8, 3) == 0
 
@@ -198,7 +214,7 @@ def test_fp8_argument_errors(attn):
     # 16 heads x 173 query tiles against 690 key tiles leave 208 tiles in the last round of 256 CUs
     # (the CPU build assumes 256): room for the balanced tail after V^T; 16 x 16 tiles fill it
     vt = 16 * 690 * 8192
-    tail = 2 * 256 * 256 * 128 * 4 + 2 * 256 * 256 * 4
+    tail = _tail_room(256 + 208)  # a slot per run (one per CU) and per tail tile
     assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + tail
     assert lib.attn_fp8_workspace_size(1, 16, 4096, 44160, 128) == vt
 

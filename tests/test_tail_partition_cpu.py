@@ -1,13 +1,22 @@
-"""The balanced tail's partition (host-side property check of its index formulas).
+"""The balanced tail's partition and the persistent launch's work queues (host-side property
+checks of their index formulas).
 
-The bf16 kernel's tail spreads U = n_tail * T units (query tile, key tile) over P workgroups:
-workgroup w takes [floor(U w / P), floor(U (w+1) / P)) and splits it at query-tile boundaries
-into at most two segments, segment i going to slot 2w + i.  The fix-up finds the runs of tail
-tile j starting from w0 = floor(((jT + 1) P - 1) / U), the last workgroup starting at or before
-jT, and reads slot 2w + (1 if the run started before jT else 0).  These formulas are restated
-here and checked for every case: each unit is computed exactly once, no run has a third
-segment, and the fix-up finds exactly the runs that cover each tile, with the slots the kernel
-wrote.
+The forward kernels' tail spreads U = n_tail * T units (query tile, key tile) over P runs: run w
+takes [floor(U w / P), floor(U (w+1) / P)) and splits it at query-tile boundaries into at most
+two segments.  Segment 0 goes to slot w; a segment 1, which starts at the first unit of tail
+tile j, to slot P + j - 1.  The fix-up finds the runs of tail tile j starting from
+w0 = floor(((jT + 1) P - 1) / U), the last run starting at or before jT, and reads slot
+P + j - 1 for the run that started before jT, slot w for the others.  These formulas are
+restated here and checked for every case: each unit is computed exactly once, no run has a third
+segment, no two segments share a slot, and the fix-up finds exactly the runs that cover each
+tile, with the slots the kernel wrote.  P is one run per CU, or up to four when the launch is
+persistent.
+
+A persistent launch of G workgroups gives workgroup g item g first; the other items are dealt
+by b % 8 over 8 queues of whole query tiles and 8 of tail runs, and a workgroup takes from its
+own XCD's whole-tile queue, the other whole-tile queues, then the tail queues.  Simulated with
+workgroups on random XCDs asking in random order: every item is taken exactly once, and no
+workgroup takes a whole tile after a tail run.
 """
 import itertools
 import random
@@ -19,8 +28,12 @@ def sk_start(U, w, P):
     return U * w // P
 
 
+def sk_slot(w, seg, j, P):
+    return w if seg == 0 else P + j - 1
+
+
 def kernel_segments(U, T, P, w):
-    """(tile, first key tile, key tiles, slot) of workgroup w, as the kernel's segment loop."""
+    """(tile, first key tile, key tiles, slot) of run w, as the kernel's segment loop."""
     u0, u1 = sk_start(U, w, P), sk_start(U, w + 1, P)
     out = []
     for seg in itertools.count():
@@ -29,7 +42,7 @@ def kernel_segments(U, T, P, w):
         s1 = (min(u1, cut)) if seg == 0 else u1
         if seg > 1 or s0 >= s1:
             break
-        out.append((s0 // T, s0 % T, s1 - s0, 2 * w + seg))
+        out.append((s0 // T, s0 % T, s1 - s0, sk_slot(w, seg, s0 // T, P)))
     return out
 
 
@@ -43,14 +56,14 @@ def fixup_runs(U, T, P, j):
         if u0 >= t1:
             break
         if u1 != u0:
-            slots.append(2 * w + (1 if u0 < t0 else 0))
+            slots.append(sk_slot(w, 1 if u0 < t0 else 0, j, P))
         w += 1
     return slots
 
 
-def plan(n_tail, T, cus=256):
+def plan(n_tail, T, cus=256, runs_per_cu=1):
     U = n_tail * T
-    return U, min(cus, U)
+    return U, min(cus * runs_per_cu, U)
 
 
 CASES = [(1, 16), (3, 79), (3, 141), (44, 79), (96, 690), (176, 72), (180, 690), (208, 696), (255, 64), (1, 2000)]
@@ -58,12 +71,14 @@ rng = random.Random(7)
 CASES += [(rng.randint(1, 255), rng.randint(16, 800)) for _ in range(40)]
 
 
+@pytest.mark.parametrize("runs_per_cu", [1, 2, 4])
 @pytest.mark.parametrize("n_tail,T", CASES)
-def test_every_unit_once_and_fixup_finds_the_runs(n_tail, T):
-    U, P = plan(n_tail, T)
+def test_every_unit_once_and_fixup_finds_the_runs(n_tail, T, runs_per_cu):
+    U, P = plan(n_tail, T, runs_per_cu=runs_per_cu)
     assert P > n_tail                      # the launcher's condition: runs of at most T units
     covered = [0] * U
     by_tile = {}
+    slots = []
     for w in range(P):
         segs = kernel_segments(U, T, P, w)
         assert len(segs) <= 2
@@ -72,7 +87,9 @@ def test_every_unit_once_and_fixup_finds_the_runs(n_tail, T):
             for u in range(tile * T + g0, tile * T + g0 + n):
                 covered[u] += 1
             by_tile.setdefault(tile, []).append(slot)
+            slots.append(slot)
     assert all(c == 1 for c in covered)
+    assert len(set(slots)) == len(slots) and 0 <= min(slots) and max(slots) < P + n_tail
     for j in range(n_tail):
         assert sorted(fixup_runs(U, T, P, j)) == sorted(by_tile[j]), j
 
@@ -82,3 +99,50 @@ def test_first_workgroup_formula_is_the_last_start_at_or_before():
         for x in range(U):
             w = ((x + 1) * P - 1) // U
             assert sk_start(U, w, P) <= x and (w + 1 == P or sk_start(U, w + 1, P) > x)
+
+
+def wq_next(counters, xcd, G, n_whole, n_items, empty):
+    """The kernel's next item for a workgroup on XCD xcd (counters: the 16 queue counters;
+    empty: the set of queues this workgroup found empty)."""
+    for k in range(16):
+        x = (xcd + k) & 7
+        qi = (k & 8) | x
+        lo = G if k < 8 else max(G, n_whole)
+        hi = n_whole if k < 8 else n_items
+        first = lo + ((x - lo) & 7)
+        if qi in empty:
+            continue
+        if first < hi:
+            b = first + 8 * counters[qi]
+            counters[qi] += 1
+            if b < hi:
+                return b
+        empty.add(qi)
+    return -1
+
+
+QUEUE_CASES = [(256, 2560, 2816), (256, 2768, 2768), (256, 256, 1280), (256, 96, 1120), (256, 352, 352),
+               (256, 300, 300), (200, 150, 1000), (256, 257, 257), (256, 0, 1024), (37, 100, 350)]
+QUEUE_CASES += [(rng.choice([8, 64, 256, 255]), rng.randint(0, 900), 0) for _ in range(20)]
+
+
+@pytest.mark.parametrize("G,n_whole,n_items", QUEUE_CASES)
+def test_persistent_queues_hand_out_every_item_once(G, n_whole, n_items):
+    n_items = max(n_items, n_whole)
+    G = min(G, n_items) if n_items else G
+    r = random.Random(G * 7919 + n_whole * 31 + n_items)
+    counters = [0] * 16
+    taken = list(range(min(G, n_items)))           # the first round: workgroup g takes item g
+    alive = {g: (r.randrange(8), set(), g >= n_whole) for g in range(min(G, n_items))}
+    while alive:
+        g = r.choice(list(alive))
+        xcd, empty, had_tail = alive[g]
+        b = wq_next(counters, xcd, G, n_whole, n_items, empty)
+        if b < 0:
+            del alive[g]
+            continue
+        assert not (had_tail and b < n_whole), "a whole tile after a tail run"
+        alive[g] = (xcd, empty, had_tail or b >= n_whole)
+        taken.append(b)
+    assert sorted(taken) == list(range(n_items))
+    assert all(c <= n_items + 16 * G for c in counters)  # no runaway counter
