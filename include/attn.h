@@ -178,7 +178,7 @@ size_t attn_shard_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t D, in
  *              A bf16 launch of several rounds of query tiles and at least
  *              512 key tiles of work per CU runs persistent: one workgroup
  *              per CU takes whole query tiles, then the tail's runs (up to
- *              4 per CU, each at least 64 key tiles), from per-XCD work
+ *              4 per CU, each at least 128 key tiles), from per-XCD work
  *              queues in the workspace, so that the XCDs end together
  *              whatever their clocks.  Which workgroup takes an item does
  *              not change the result.

@@ -129,14 +129,18 @@ int device_cus() {
 // tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).  The FP8
 // kernel's tiles take half the time, so its fixed costs weigh about twice as many tiles.
 //
-// A launch of several rounds runs the bf16 kernel persistent (FwdArgs::persist): one workgroup
-// per CU taking items from per-XCD work queues, so that the fast XCDs take over the slow ones'
-// remaining work (the XCDs' clocks differ by up to ~8%, and a static grid ends with the slowest
-// XCD).  Its tail is then cut into up to kSkMaxRunsPerCu runs per CU, each at least
-// kSkMinRunTiles key tiles long, so that the end balances to a fraction of a query tile; the
-// queues' extra cost (a few microseconds per item) pays off from about kPersistMinTiles key
-// tiles per CU (44,160-key shares: 4-7% faster on the slowest boxes seen, 0.5-1% on the
-// fastest; the 4,608-token image shape, 121 tiles per CU, ran 3-10% slower persistent).
+// A launch of several rounds runs persistent (FwdArgs::persist): one workgroup per CU taking
+// items from per-XCD work queues, so that the fast XCDs take over the slow ones' remaining work
+// (the XCDs' clocks differ by up to ~8%, and a static grid ends with the slowest XCD).  Its tail
+// is then cut into up to kSkMaxRunsPerCu runs per CU, each at least kSkMinRunTiles key tiles
+// long, so that the end balances to a fraction of a query tile.  A run's fixed costs (its
+// prologue, epilogue, fp32 partial and the queue) come to about 9 us: at 65 key tiles per run
+// (the ring share cut 4 ways) they outweighed the balance gained on a box whose XCDs were
+// close (2.5% slower), at 140 (the full sequence) they did not (1% faster); on the slowest
+// boxes seen the finer tail gained 4% at either.  The queues' extra cost (a few microseconds
+// per item) pays off from about kPersistMinTiles key tiles per CU (44,160-key shares: 4-7%
+// faster on the slowest boxes, 1% on the fastest; the 4,608-token image shape, 121 tiles per
+// CU, ran 3-10% slower persistent).
 struct SkPlan {
     int n_dp = 0;    // query tiles run whole
     int sk_wgs = 0;  // runs of the tail (0 = no tail)
@@ -144,17 +148,19 @@ struct SkPlan {
 constexpr int64_t kSkMinSavingBf16 = 40;
 constexpr int64_t kSkMinSavingFp8 = 64;
 constexpr int kSkMaxRunsPerCu = 4;
-constexpr int64_t kSkMinRunTiles = 64;
+constexpr int64_t kSkMinRunTiles = 128;
 constexpr int64_t kPersistMinTiles = 512;
 
-// runs_per_cu: the most runs per CU (1 for a launch of one workgroup per item)
-SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int runs_per_cu = 1) {
+// runs_per_cu: the most runs per CU (1 for a launch of one workgroup per item), min_run: the
+// fewest key tiles per run when there are more
+SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int runs_per_cu = 1,
+               int64_t min_run = kSkMinRunTiles) {
     SkPlan p;
     if (n_q <= 0 || T <= 0 || cus <= 0 || n_q > 0x7FFFFFFF) return p;
     const int64_t rem = n_q % cus;
     if (rem == 0 || T * (cus - rem) / cus < min_saving) return p;
     const int64_t U = rem * T;  // > rem, since T > min_saving >= 1: every run is at most T long
-    int64_t k = U / ((int64_t)cus * kSkMinRunTiles);
+    int64_t k = U / ((int64_t)cus * min_run);
     k = k < 1 ? 1 : (k > runs_per_cu ? runs_per_cu : k);
     const int dk = debug_tail_runs();
     if (runs_per_cu > 1 && dk > 0) k = dk;
@@ -180,12 +186,29 @@ size_t tail_room(int64_t n_q, int cus, int D) {
     return sk_bytes((n_q > cus ? kSkMaxRunsPerCu : 1) * (int64_t)cus + rem, D);
 }
 
-// The FP8 call's workspace: V^T tiles, then the balanced tail's partials when it runs.
+// The persistent launch and its tail for a launch of n_q query tiles against T key tiles: bf16
+// (weight 1) or FP8, whose tiles take about half the time (weight 2: twice the tiles per CU
+// before the queues pay, twice the key tiles per run).  persist_ok: the caller has room for the
+// work queues.
+struct LaunchPlan {
+    bool persist = false;
+    SkPlan sk;
+};
+LaunchPlan launch_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int64_t weight, bool persist_ok) {
+    LaunchPlan lp;
+    lp.persist = persist_ok && n_q > cus && n_q * T >= kPersistMinTiles * weight * cus;
+    if (debug_persist() >= 0) lp.persist = persist_ok && n_q > cus && debug_persist() == 1;
+    lp.sk = sk_plan(n_q, T, cus, min_saving, lp.persist ? kSkMaxRunsPerCu : 1, kSkMinRunTiles * weight);
+    return lp;
+}
+
+// The FP8 call's workspace: V^T tiles, then, for a persistent launch, the work queues, then the
+// balanced tail's partials when it runs.
 size_t fp8_vt_bytes(int64_t B, int64_t H, int32_t Skv) {
     return (size_t)B * H * lsdit::fp8_key_tiles(Skv) * lsdit::kFp8TileBytes;
 }
-SkPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
-    return sk_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus(), kSkMinSavingFp8);
+LaunchPlan fp8_plan(int64_t B, int64_t H, int64_t Sq, int32_t Skv) {
+    return launch_plan(n_qtiles(B, H, Sq), lsdit::fp8_key_tiles(Skv), device_cus(), kSkMinSavingFp8, 2, true);
 }
 
 // fp32 chunk slots of a schedule: NWAY keeps every chunk's partial, ONLINE one running result
@@ -338,13 +361,12 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
     // into the output.
     auto launch = [&](FwdArgs a, int64_t T) -> attn_status_t {
         const bool bf16 = in_dt == ATTN_BF16;
-        bool persist = bf16 && wq && n_q * T >= kPersistMinTiles * cus;
-        if (debug_persist() >= 0) persist = bf16 && wq && debug_persist() == 1;
-        if (persist) {
+        const LaunchPlan lp = bf16 ? launch_plan(n_q, T, tail_cus, kSkMinSavingBf16, 1, wq != nullptr) : LaunchPlan{};
+        if (lp.persist) {
             a.persist = cus;
             a.wq = wq;
         }
-        const SkPlan p = bf16 ? sk_plan(n_q, T, tail_cus, kSkMinSavingBf16, persist ? kSkMaxRunsPerCu : 1) : SkPlan{};
+        const SkPlan& p = lp.sk;
         const int64_t n_slots = sk_slots(p, n_q);
         void* tw = tail_ws;
         size_t tb = tail_bytes;
@@ -537,8 +559,9 @@ attn_status_t attn_ulysses_unpack(const void* packed, attn_dtype_t dt, int32_t B
 
 size_t attn_fp8_workspace_size(int32_t B, int32_t H, int32_t Sq, int32_t Skv, int32_t D) {
     if (B <= 0 || H <= 0 || Sq < 0 || Skv <= 0 || D != 128) return 0;
-    const SkPlan p = fp8_plan(B, H, Sq, Skv);
-    return fp8_vt_bytes(B, H, Skv) + (p.sk_wgs ? sk_bytes(sk_slots(p, n_qtiles(B, H, Sq)), D) : 0);
+    const LaunchPlan lp = fp8_plan(B, H, Sq, Skv);
+    return fp8_vt_bytes(B, H, Skv) + (lp.persist ? kWqBytes : 0) +
+           (lp.sk.sk_wgs ? sk_bytes(sk_slots(lp.sk, n_qtiles(B, H, Sq)), D) : 0);
 }
 
 attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k, attn_strides_t ks, const void* v,
@@ -578,12 +601,20 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     a.v_descale = v_descale;
     a.wg_order = debug_wg_order();
     if (!(a.c > 0.f) || !isfinite(a.c)) return ATTN_ERR_SHAPE;
-    // the balanced tail, as in attn_shard_fwd, its partials after V^T in the workspace
-    const SkPlan p = fp8_plan(B, H, Sq, Skv);
+    // the persistent launch and the balanced tail, as in attn_shard_fwd: the work queues, then the
+    // tail's partials, after V^T in the workspace
+    const LaunchPlan lp = fp8_plan(B, H, Sq, Skv);
+    const SkPlan& p = lp.sk;
+    char* after_vt = (char*)workspace + fp8_vt_bytes(B, H, Skv);
+    if (lp.persist) {
+        a.persist = device_cus();
+        a.wq = (unsigned*)after_vt;
+        after_vt += kWqBytes;
+    }
     if (p.sk_wgs) {
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
-        a.sk_o = (float*)((char*)workspace + fp8_vt_bytes(B, H, Skv));
+        a.sk_o = (float*)after_vt;
         a.sk_lse = (float*)((char*)a.sk_o + sk_o_bytes(sk_slots(p, n_qtiles(B, H, Sq)), D));
     }
     if (lsdit::launch_fp8_pack_v(a, s) != hipSuccess) return ATTN_ERR_HIP;

@@ -131,35 +131,6 @@ __device__ __forceinline__ int v_swz(int row) {
     else return 2 * s0 + 4 * s1;
 }
 
-// The next item of a persistent workgroup on XCD xcd (FwdArgs: a grid of G workgroups took
-// items 0 .. G-1 first).  The remaining items are split by b % 8 == x, the XCD a round-robin
-// dispatch would give them (so xcd_remap's locality holds), over 8 queues of whole query tiles
-// (counter x: items G <= b < n_whole) and 8 queues of tail runs (counter 8 + x: items
-// max(G, n_whole) <= b < n_items), each handed out in increasing order.  The workgroup takes
-// from its own XCD's whole-tile queue, then from the others' (the longest items go first), then
-// from the tail queues in the same order; -1 when all are empty.  A queue found empty is marked
-// in `empty` and not asked again.  Relaxed atomics: an item only needs a unique index, and
-// items write disjoint outputs.
-__device__ __forceinline__ int wq_next(unsigned* wq, int xcd, int G, int n_whole, int n_items, unsigned& empty) {
-#pragma unroll 1
-    for (int k = 0; k < 16; ++k) {
-        const int x = (xcd + k) & 7, qi = (k & 8) | x;
-        const int lo = k < 8 ? G : (G > n_whole ? G : n_whole), hi = k < 8 ? n_whole : n_items;
-        const int first = lo + ((x - lo) & 7);  // the queue's first item
-        if ((empty >> qi) & 1u) continue;
-        if (first < hi) {
-            const int b = first + 8 * (int)atomicAdd(wq + qi * kWorkQueueStride, 1u);
-            if (b < hi) return b;
-        }
-        empty |= 1u << qi;
-    }
-    return -1;
-}
-
-__global__ void wq_clear_kernel(unsigned* wq) {
-    if (threadIdx.x < kWorkQueueWords / kWorkQueueStride) wq[threadIdx.x * kWorkQueueStride] = 0u;
-}
-
 // Workgroups are dispatched to the 8 XCDs round-robin; give XCD x a contiguous
 // range of logical tiles so its concurrently resident workgroups share K/V.
 __device__ __forceinline__ int xcd_remap(int bid, int n) {
@@ -585,17 +556,20 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
                 bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
             } else {
                 if (ar.persist == 0) break;
-                // every wave is done with the last item's tiles (and no load is in flight) before
-                // the next item's prologue rewrites LDS, and has read the last broadcast
-                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-                __syncthreads();
+                // thread 0 takes the next item as soon as its wave is done (the atomic's latency
+                // overlaps the drain of the last item's stores) and broadcasts it through one of
+                // two LDS words, alternately: the other waves may still be reading the last
+                // item's word, and every wave read the older one before the last barrier
+                int* const item = (int*)(smem + C::ITEM_ADDR) + (it & 1);
                 if (tid == 0) {
                     const int xcd = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // XCC_ID[3:0]
-                    *(int*)(smem + C::ITEM_ADDR) =
-                        wq_next(ar.wq, xcd, (int)gridDim.x, n_whole, n_whole + ar.sk_wgs, wq_empty);
+                    *item = wq_next(ar.wq, xcd, (int)gridDim.x, n_whole, n_whole + ar.sk_wgs, wq_empty);
                 }
+                // every wave is done with the last item's tiles (and no load is in flight) before
+                // the next item's prologue rewrites LDS
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
                 __syncthreads();
-                bid = __builtin_amdgcn_readfirstlane(*(volatile int*)(smem + C::ITEM_ADDR));
+                bid = __builtin_amdgcn_readfirstlane(*(volatile int*)item);
                 if (bid < 0) break;
             }
         }
@@ -945,7 +919,8 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     int64_t grid = n_tiles;
     if (a.persist > 0 && n_tiles > a.persist) {
         // the queues start empty (a kernel, not a memset, so that the launch can be captured)
-        hipLaunchKernelGGL(wq_clear_kernel, dim3(1), dim3(64), 0, stream, a.wq);
+        e = launch_wq_clear(a.wq, stream);
+        if (e != hipSuccess) return e;
         grid = a.persist;
     } else {
         ka.persist = 0;  // one round: every item has its own workgroup

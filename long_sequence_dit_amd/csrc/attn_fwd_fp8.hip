@@ -65,7 +65,8 @@ constexpr int BK = 64;              // keys per tile
 constexpr int K_ROW = D;            // bytes per K row
 constexpr int TILE = kFp8TileBytes; // bytes of a K tile and of a V^T tile
 constexpr int NSTAGE = 4;           // LDS buffers per tensor (the key loop is unrolled by NSTAGE)
-constexpr int LDS_BYTES = 2 * NSTAGE * TILE;
+constexpr int ITEM_ADDR = 2 * NSTAGE * TILE;  // a persistent workgroup's next item, broadcast to the waves
+constexpr int LDS_BYTES = ITEM_ADDR + 16;
 constexpr int BLKS = TILE / 1024;   // wave-wide 1 KiB loads per tile
 constexpr int LOADERS = NW / 2;     // waves 0-3 issue the tile loads (as in the bf16 kernel)
 constexpr int BLKS_PER_WAVE = BLKS / LOADERS;
@@ -407,31 +408,59 @@ __device__ __forceinline__ void stream(Wave& w, const Addr& ad, unsigned v0, uns
 }
 
 __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int n_kt) {
-    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-    (void)smem;  // no static LDS: the dynamic block starts at LDS address 0
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];  // no static LDS: starts at address 0
     static_assert(BQ == kSkRows, "stream-K slots hold one query tile");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_q = a.B * a.H * n_qt;
 
-    // This workgroup's segments (query tile, run of key tiles): one whole query tile, or, for a
-    // workgroup of the balanced tail (see Fp8Args), its run of (query tile, key tile) units,
-    // which spans at most two query tiles.  As in the bf16 kernel, each iteration re-derives its
-    // segment, the arguments (through an opaque pointer) and the lane index, so nothing computed
-    // from them is held across the key loop, and the segment bounds are made wave-uniform.
-    for (int seg = 0;; ++seg) {
+    // This workgroup's items (see Fp8Args, FwdArgs), each one or two segments (query tile, run of
+    // key tiles): a whole query tile, or a run of the balanced tail's (query tile, key tile)
+    // units, which spans at most two query tiles.  The first item is the workgroup's own index; a
+    // persistent workgroup then takes items from the work queues (wq_next) until they are
+    // empty.  As in the bf16 kernel, each iteration re-derives its segment, the arguments
+    // (through an opaque pointer) and the lane index, so nothing computed from them is held
+    // across the key loop, and the segment bounds are made wave-uniform.
+    int seg = 0, bid = 0;
+    unsigned wq_empty = 0;  // queues found empty (thread 0's)
+    for (int it = 0;; ++it) {
         const kernarg_t<Fp8Args>* ap = (const kernarg_t<Fp8Args>*)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
         const kernarg_t<Fp8Args>& ar = *ap;
-        const int bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
+        const int n_whole = ar.sk_wgs == 0 ? n_q : ar.n_dp;
+        if (seg == 0) {
+            if (it == 0) {
+                bid = wg_logical((int)blockIdx.x, (int)gridDim.x, ar.wg_order);
+            } else {
+                if (ar.persist == 0) break;
+                // thread 0 takes the next item as soon as its wave is done (the atomic's latency
+                // overlaps the drain of the last item's stores) and broadcasts it through one of
+                // two LDS words, alternately: the other waves may still be reading the last
+                // item's word, and every wave read the older one before the last barrier
+                int* const item = (int*)(smem + ITEM_ADDR) + (it & 1);
+                if (tid == 0) {
+                    const int xcd = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // XCC_ID[3:0]
+                    *item = wq_next(ar.wq, xcd, (int)gridDim.x, n_whole, n_whole + ar.sk_wgs, wq_empty);
+                }
+                // every wave is done with the last item's tiles (and no load is in flight) before
+                // the next item's prologue rewrites LDS
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                __syncthreads();
+                bid = __builtin_amdgcn_readfirstlane(*(volatile int*)item);
+                if (bid < 0) break;
+            }
+        }
         int lane = tid & 63;
         asm volatile("" : "+v"(lane));
         const int hi = lane >> 5;
         int sk_slot_ = -1, gidx, g_first, nkt;
-        if (ar.sk_wgs == 0 || bid < ar.n_dp) {
-            if (seg > 0) break;
-            gidx = xcd_remap(bid, ar.sk_wgs == 0 ? n_q : ar.n_dp);
+        if (bid < n_whole) {
+            if (seg > 0) {
+                seg = 0;
+                continue;
+            }
+            gidx = xcd_remap(bid, n_whole);
             g_first = 0;
             nkt = n_kt;
         } else {
@@ -445,7 +474,10 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
             const int64_t cut = (u0 / n_kt + 1) * n_kt;
             const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
-            if (seg > 1 || s0 >= s1) break;
+            if (seg > 1 || s0 >= s1) {
+                seg = 0;
+                continue;
+            }
             sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / n_kt), ar.sk_wgs);
             gidx = ar.n_dp + (int)(s0 / n_kt);
             g_first = (int)(s0 % n_kt);
@@ -461,6 +493,7 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             __syncthreads();
         }
+        ++seg;
         const int bh = gidx / n_qt, qt = gidx % n_qt;
         const int b = bh / ar.H, h = bh % ar.H;
         const unsigned char* qp = (const unsigned char*)ar.q + b * ar.qs.b + h * ar.qs.h;
@@ -710,7 +743,7 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
             return hipErrorInvalidValue;
         blocks = (int64_t)a.n_dp + a.sk_wgs;
     }
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (blocks > 0x7FFFFFFF || a.persist < 0 || (a.persist > 0 && !a.wq)) return hipErrorInvalidValue;
     // per device: the kernel's dynamic LDS limit has been raised (an atomic flag, so that
     // first calls from several threads are safe: each may set the attribute, which is idempotent)
     static std::atomic<bool> attr_set[64];
@@ -722,7 +755,16 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) attr_set[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)blocks), dim3(NT), LDS_BYTES, stream, a, n_qt, n_kt);
+    Fp8Args ka = a;
+    int64_t grid = blocks;
+    if (a.persist > 0 && blocks > a.persist) {
+        e = launch_wq_clear(a.wq, stream);  // the queues start empty
+        if (e != hipSuccess) return e;
+        grid = a.persist;
+    } else {
+        ka.persist = 0;  // one round: every item has its own workgroup
+    }
+    hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)grid), dim3(NT), LDS_BYTES, stream, ka, n_qt, n_kt);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ struct FwdArgs {
     int sk_wgs;          // runs of the tail; 0 = no tail
     float* sk_o;
     float* sk_lse;
-    // Dispatch (bf16 path).  persist == 0: one workgroup per item.  persist > 0: a persistent
+    // Dispatch.  persist == 0: one workgroup per item.  persist > 0: a persistent
     // grid of min(n_items, persist) workgroups (one per CU); workgroup g takes item g, then
     // further items from the work queues in wq (kWorkQueueWords words, zeroed before the
     // launch), until they are empty.  Results do not depend on which workgroup takes an item.
@@ -108,6 +108,31 @@ __host__ __device__ inline int sk_slot(int w, int seg, int j, int n_runs) { retu
 constexpr int kWorkQueueStride = 64;
 constexpr int kWorkQueueWords = 16 * kWorkQueueStride;
 
+// The next item of a persistent workgroup on XCD xcd (FwdArgs::persist: a grid of G
+// workgroups took items 0 .. G-1 first).  The remaining items are split by b % 8 == x, the XCD a round-robin
+// dispatch would give them (so xcd_remap's locality holds), over 8 queues of whole query tiles
+// (counter x: items G <= b < n_whole) and 8 queues of tail runs (counter 8 + x: items
+// max(G, n_whole) <= b < n_items), each handed out in increasing order.  The workgroup takes
+// from its own XCD's whole-tile queue, then from the others' (the longest items go first), then
+// from the tail queues in the same order; -1 when all are empty.  A queue found empty is marked
+// in `empty` and not asked again.  Relaxed atomics: an item only needs a unique index, and
+// items write disjoint outputs.
+__device__ __forceinline__ int wq_next(unsigned* wq, int xcd, int G, int n_whole, int n_items, unsigned& empty) {
+#pragma unroll 1
+    for (int k = 0; k < 16; ++k) {
+        const int x = (xcd + k) & 7, qi = (k & 8) | x;
+        const int lo = k < 8 ? G : (G > n_whole ? G : n_whole), hi = k < 8 ? n_whole : n_items;
+        const int first = lo + ((x - lo) & 7);  // the queue's first item
+        if ((empty >> qi) & 1u) continue;
+        if (first < hi) {
+            const int b = first + 8 * (int)atomicAdd(wq + qi * kWorkQueueStride, 1u);
+            if (b < hi) return b;
+        }
+        empty |= 1u << qi;
+    }
+    return -1;
+}
+
 // Merge of the stream-K partials of query tiles n_dp .. n_q-1 (see FwdArgs).
 struct SkFixupArgs {
     int B, H, Sq, D;
@@ -165,11 +190,14 @@ struct Fp8Args {
     int B, H, Sq, Skv;   // Skv >= 1
     float c;             // scale * log2(e) * q_descale * k_descale
     float v_descale;
-    // Balanced tail, as in FwdArgs (query tiles of kSkRows rows, T = fp8_key_tiles(Skv))
+    // Balanced tail and dispatch, as in FwdArgs (query tiles of kSkRows rows,
+    // T = fp8_key_tiles(Skv))
     int n_dp;
-    int sk_wgs;          // 0 = no stream-K tail
+    int sk_wgs;          // runs of the tail; 0 = no tail
     float* sk_o;
     float* sk_lse;
+    int persist;
+    unsigned* wq;
     int wg_order;        // as in FwdArgs
 };
 int fp8_key_tiles(int Skv);
@@ -179,6 +207,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_sk_fixup(const SkFixupArgs& a, hipStream_t stream);
+// Zeroes the kWorkQueueWords-word work queues of a persistent launch (a kernel, not a memset).
+hipError_t launch_wq_clear(unsigned* wq, hipStream_t stream);
 hipError_t launch_fp8_pack_v(const Fp8Args& a, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 // O = 0 and LSE = -inf for every row (a chunk without keys).

@@ -213,6 +213,16 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+__global__ void wq_clear_kernel(unsigned* wq) {
+    if (threadIdx.x < kWorkQueueWords / kWorkQueueStride) wq[threadIdx.x * kWorkQueueStride] = 0u;
+}
+
+hipError_t launch_wq_clear(unsigned* wq, hipStream_t stream) {
+    if (!wq) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(wq_clear_kernel, dim3(1), dim3(64), 0, stream, wq);
+    return hipGetLastError();
+}
+
 hipError_t launch_sk_fixup(const SkFixupArgs& a, hipStream_t stream) {
     const int n_tail = a.n_q - a.n_dp;
     if (n_tail <= 0) return hipSuccess;

@@ -214,8 +214,9 @@ def test_fp8_argument_errors(attn):
     # 16 heads x 173 query tiles against 690 key tiles leave 208 tiles in the last round of 256 CUs
     # (the CPU build assumes 256): room for the balanced tail after V^T; 16 x 16 tiles fill it
     vt = 16 * 690 * 8192
-    tail = _tail_room(256 + 208)  # a slot per run (one per CU) and per tail tile
-    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + tail
+    # a persistent launch (2768 tiles x 690 key tiles): the work queues, then a slot per run (2 per
+    # CU: 143,520 units, each run at least 256 FP8 key tiles) and per tail tile
+    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + WQ + _tail_room(2 * 256 + 208)
     assert lib.attn_fp8_workspace_size(1, 16, 4096, 44160, 128) == vt
 
     def f(q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=need, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1, dq=1.0, dk=1.0,
@@ -242,14 +243,17 @@ def test_fp8_argument_errors(attn):
 
 
 def test_bench_tail_rule_matches_the_library(attn):
-    """bench.py reports which kernels a step launches with its own copy of the balanced tail's
-    rule; the FP8 workspace size (V^T tiles, plus the tail's slots exactly when the tail runs)
-    shows the library's decision, which must agree for every shape (256 CUs on the CPU build)."""
+    """bench.py reports which kernels a step launches with its own copies of the balanced tail's
+    and the persistent launch's rules; the FP8 workspace size (V^T tiles, plus the work queues
+    exactly when the launch is persistent, plus the tail's slots exactly when the tail runs)
+    shows the library's decisions, which must agree for every shape (256 CUs on the CPU build)."""
     import bench
     lib = attn.load()
     for B, H, Sq, Skv in [(1, 16, 44160, 44160), (1, 4, 44160, 44160), (1, 16, 5520, 44160), (1, 24, 4608, 4608),
                           (1, 16, 4096, 44160), (1, 3, 200, 5000), (1, 3, 200, 3000), (1, 2, 10, 20),
-                          (2, 7, 1000, 9000), (1, 1, 300, 8323072)]:
+                          (2, 7, 1000, 9000), (1, 1, 300, 8323072), (1, 32, 4096, 44160), (1, 40, 4096, 3000)]:
         vt = B * H * -(-Skv // 64) * 8192
-        runs = lib.attn_fp8_workspace_size(B, H, Sq, Skv, 128) > vt
-        assert runs == bench.tail_runs(B * H * -(-Sq // 256), -(-Skv // 64), 256), (B, H, Sq, Skv)
+        n_q, T = B * H * -(-Sq // 256), -(-Skv // 64)
+        extra = lib.attn_fp8_workspace_size(B, H, Sq, Skv, 128) - vt - (WQ if bench.persistent_launch(n_q, T, 256, 2) else 0)
+        assert extra >= 0 and extra % 256 == 0, (B, H, Sq, Skv)
+        assert (extra > 0) == bench.tail_runs(n_q, T, 256), (B, H, Sq, Skv)
