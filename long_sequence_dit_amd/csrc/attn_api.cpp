@@ -96,9 +96,10 @@ int debug_wg_order() {
     return 0;
 }
 
-// Debug aids for tests: LSDIT_DEBUG_PERSIST=0 never runs the bf16 kernel persistent, =1 does so
-// for every launch of more than one round (whatever its work per CU); LSDIT_DEBUG_TAIL_RUNS=k
-// (1..kSkMaxRunsPerCu) fixes a persistent launch's tail runs per CU.  -1: not set.
+// Debug aids for tests: LSDIT_DEBUG_PERSIST=0 never runs a launch persistent, =1 does so for
+// every launch of more than one round (whatever its work per CU); LSDIT_DEBUG_TAIL fixes a
+// persistent launch's tail: "ranges" for one run of equal units per CU (as a launch of one
+// workgroup per item has), an integer r >= 2 for r parts per tail tile.  -1: not set.
 int debug_persist() {
     const char* e = getenv("LSDIT_DEBUG_PERSIST");
     if (!e) return -1;
@@ -106,11 +107,12 @@ int debug_persist() {
     if (strcmp(e, "1") == 0) return 1;
     return -1;
 }
-int debug_tail_runs() {
-    const char* e = getenv("LSDIT_DEBUG_TAIL_RUNS");
+int debug_tail() {
+    const char* e = getenv("LSDIT_DEBUG_TAIL");
     if (!e) return -1;
-    const int k = atoi(e);
-    return k >= 1 && k <= 4 ? k : -1;
+    if (strcmp(e, "ranges") == 0) return 0;
+    const int r = atoi(e);
+    return r >= 2 ? r : -1;
 }
 
 int device_cus() {
@@ -120,30 +122,34 @@ int device_cus() {
     return n;
 }
 
-// The balanced tail of the bf16 kernel (FwdArgs): when its n_q query tiles leave CUs idle in
-// the last round, the full rounds run whole query tiles and the last round's work is spread
-// evenly over the CUs as runs of (query tile, key tile) units, whose partials the fix-up kernel
-// merges.  Worth it when the idle part of the last round is at least min_saving key tiles per
-// CU: the runs' pipeline fill and drain, their partials and the fix-up launch cost about as much
-// as 20-30 key tiles (bf16: at 22 tiles, the 4,608-token image shape ran 4.5% slower with the
-// tail; at 200-430 tiles the 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).  The FP8
-// kernel's tiles take half the time, so its fixed costs weigh about twice as many tiles.
-//
-// A launch of several rounds runs persistent (FwdArgs::persist): one workgroup per CU taking
-// items from per-XCD work queues, so that the fast XCDs take over the slow ones' remaining work
-// (the XCDs' clocks differ by up to ~8%, and a static grid ends with the slowest XCD).  Its tail
-// is then cut into up to kSkMaxRunsPerCu runs per CU, each at least kSkMinRunTiles key tiles
-// long, so that the end balances to a fraction of a query tile.  A run's fixed costs (its
-// prologue, epilogue, fp32 partial and the queue) come to about 9 us: at 65 key tiles per run
-// (the ring share cut 4 ways) they outweighed the balance gained on a box whose XCDs were
-// close (2.5% slower), at 140 (the full sequence) they did not (1% faster); on the slowest
-// boxes seen the finer tail gained 4% at either.  The queues' extra cost (a few microseconds
-// per item) pays off from about kPersistMinTiles key tiles per CU (44,160-key shares: 4-7%
-// faster on the slowest boxes, 1% on the fastest; the 4,608-token image shape, 121 tiles per
-// CU, ran 3-10% slower persistent).
+// The balanced tail (FwdArgs): when a launch's n_q query tiles leave CUs idle in the last round,
+// the full rounds run whole query tiles and the last round's work is spread over the CUs as runs
+// of (query tile, key tile) units, whose partials the fix-up kernel merges.  Worth it when the
+// idle part of the last round is at least min_saving key tiles per CU: the runs' pipeline fill
+// and drain, their partials and the fix-up launch cost about as much as 20-30 key tiles (bf16:
+// at 22 tiles, the 4,608-token image shape ran 4.5% slower with the tail; at 200-430 tiles the
+// 44,160-key Ulysses and ring shares ran 2.7-2.8% faster).  The FP8 kernel's tiles take half the
+// time, so its fixed costs weigh about twice as many tiles.
+//  * A launch of one workgroup per item cuts the tail into one run of equal units per CU: the
+//    hardware deals the runs out as CUs come free, and equal runs end together.
+//  * A persistent launch (FwdArgs::persist) cuts every tail tile into r equal parts instead, r
+//    as large as runs of at least min_run key tiles and at most kSkMaxRunsPerCu runs per CU
+//    allow, so that its queues balance the end to a fraction of a query tile, given at least one
+//    run per CU (else one run of equal units per CU, as above).  A run's fixed costs (prologue,
+//    epilogue, fp32 partial, the queue) come to about 9 us: at 65 key tiles per run (the ring
+//    share, runs of equal units cut 4 ways) they outweighed the balance gained on a box whose
+//    XCDs were close (2.5% slower), at 140 (the full sequence) they did not (1% faster); on the
+//    slowest boxes seen the finer tail gained 4% at either.  Parts, unlike runs of equal units,
+//    never cross a tile boundary, and the queues hand them out part-major, so that an XCD's runs
+//    at one time read the same key range.
+// The persistent launch itself pays off from about kPersistMinTiles key tiles per CU (its
+// queues cost a few microseconds per item): the XCDs' clocks differ by up to ~8%, and a static
+// grid ends with the slowest XCD (44,160-key shares: 4-7% faster on the slowest boxes, 1% on the
+// fastest; the 4,608-token image shape, 121 tiles per CU, ran 3-10% slower persistent).
 struct SkPlan {
     int n_dp = 0;    // query tiles run whole
     int sk_wgs = 0;  // runs of the tail (0 = no tail)
+    int parts = 0;   // 0: runs of equal units; r >= 2: r parts per tail tile
 };
 constexpr int64_t kSkMinSavingBf16 = 40;
 constexpr int64_t kSkMinSavingFp8 = 64;
@@ -151,35 +157,45 @@ constexpr int kSkMaxRunsPerCu = 4;
 constexpr int64_t kSkMinRunTiles = 128;
 constexpr int64_t kPersistMinTiles = 512;
 
-// runs_per_cu: the most runs per CU (1 for a launch of one workgroup per item), min_run: the
-// fewest key tiles per run when there are more
-SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int runs_per_cu = 1,
+// persist: the launch is persistent; min_run: the fewest key tiles per part
+SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, bool persist = false,
                int64_t min_run = kSkMinRunTiles) {
     SkPlan p;
     if (n_q <= 0 || T <= 0 || cus <= 0 || n_q > 0x7FFFFFFF) return p;
     const int64_t rem = n_q % cus;
     if (rem == 0 || T * (cus - rem) / cus < min_saving) return p;
     const int64_t U = rem * T;  // > rem, since T > min_saving >= 1: every run is at most T long
-    int64_t k = U / ((int64_t)cus * min_run);
-    k = k < 1 ? 1 : (k > runs_per_cu ? runs_per_cu : k);
-    const int dk = debug_tail_runs();
-    if (runs_per_cu > 1 && dk > 0) k = dk;
     p.n_dp = (int)(n_q - rem);
-    p.sk_wgs = (int)(U < cus * k ? U : cus * k);
+    p.sk_wgs = (int)(U < cus ? U : cus);
+    if (persist) {
+        const int64_t most = ((int64_t)kSkMaxRunsPerCu * cus + rem - 1) / rem;
+        int64_t r = T / min_run < most ? T / min_run : most;
+        if (r * rem < cus) r = 0;  // fewer parts than CUs: equal units balance better
+        const int dt = debug_tail();
+        if (dt >= 0) r = dt;
+        if (r >= 2 && r <= T) {
+            p.parts = (int)r;
+            p.sk_wgs = (int)(r * rem);
+        }
+    }
     return p;
 }
 
-// Query tiles of the bf16 kernel, and the workspace of its tail: one partial slot per run and
-// one per tail tile boundary (lsdit::sk_slot), each of kSkRows rows of D fp32 values and an LSE.
+// Query tiles of the bf16 kernel, and the workspace of its tail: one partial slot per run, and
+// for runs of equal units one per tail tile boundary (lsdit::sk_slot), each of kSkRows rows of D
+// fp32 values and an LSE.
 int64_t n_qtiles(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows); }
-int64_t sk_slots(const SkPlan& p, int64_t n_q) { return p.sk_wgs ? p.sk_wgs + (n_q - p.n_dp) : 0; }
+int64_t sk_slots(const SkPlan& p, int64_t n_q) {
+    return p.sk_wgs == 0 ? 0 : p.parts ? p.sk_wgs : p.sk_wgs + (n_q - p.n_dp);
+}
 size_t sk_o_bytes(int64_t n_slots, int D) { return align_up((size_t)n_slots * lsdit::kSkRows * D * 4); }
 size_t sk_bytes(int64_t n_slots, int D) { return sk_o_bytes(n_slots, D) + align_up((size_t)n_slots * lsdit::kSkRows * 4); }
 // The work queues of a persistent launch, in the workspace before the tail's partials: present
 // when the query tiles take more than one round.
 constexpr size_t kWqBytes = (size_t)lsdit::kWorkQueueWords * 4;
 size_t wq_bytes(int64_t n_q, int cus) { return n_q > cus ? kWqBytes : 0; }
-// The most room a shape's tail can take: runs of up to kSkMaxRunsPerCu per CU when persistent
+// The most room a shape's tail can take: up to kSkMaxRunsPerCu runs per CU (rounded up to whole
+// parts per tail tile) when persistent
 size_t tail_room(int64_t n_q, int cus, int D) {
     const int64_t rem = n_q % cus;
     if (rem == 0) return 0;
@@ -198,7 +214,7 @@ LaunchPlan launch_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int6
     LaunchPlan lp;
     lp.persist = persist_ok && n_q > cus && n_q * T >= kPersistMinTiles * weight * cus;
     if (debug_persist() >= 0) lp.persist = persist_ok && n_q > cus && debug_persist() == 1;
-    lp.sk = sk_plan(n_q, T, cus, min_saving, lp.persist ? kSkMaxRunsPerCu : 1, kSkMinRunTiles * weight);
+    lp.sk = sk_plan(n_q, T, cus, min_saving, lp.persist, kSkMinRunTiles * weight);
     return lp;
 }
 
@@ -378,6 +394,7 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
         if (p.sk_wgs == 0 || !tw || tb < sk_bytes(n_slots, D)) return ok(run_fwd(a, in_dt, s)) ? ATTN_OK : ATTN_ERR_HIP;
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
+        a.sk_parts = p.parts;
         a.sk_o = (float*)tw;
         a.sk_lse = (float*)((char*)tw + sk_o_bytes(n_slots, D));
         if (!ok(run_fwd(a, in_dt, s))) return ATTN_ERR_HIP;
@@ -385,7 +402,7 @@ attn_status_t shard_fwd_impl(const void* q, attn_strides_t qs, const void* k, at
         f.B = B; f.H = H; f.Sq = Sq; f.D = D;
         f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
         f.T = (int)T;
-        f.n_dp = p.n_dp; f.n_q = (int)n_q; f.sk_wgs = p.sk_wgs;
+        f.n_dp = p.n_dp; f.n_q = (int)n_q; f.sk_wgs = p.sk_wgs; f.sk_parts = p.parts;
         f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
         f.o = a.o; f.os = a.os; f.o_bf16 = a.o_bf16; f.lse = a.lse;
         f.run_o = a.run_o; f.run_lse = a.run_lse;
@@ -614,6 +631,7 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     if (p.sk_wgs) {
         a.n_dp = p.n_dp;
         a.sk_wgs = p.sk_wgs;
+        a.sk_parts = p.parts;
         a.sk_o = (float*)after_vt;
         a.sk_lse = (float*)((char*)a.sk_o + sk_o_bytes(sk_slots(p, n_qtiles(B, H, Sq)), D));
     }
@@ -624,7 +642,7 @@ attn_status_t attn_chunk_fwd_fp8(const void* q, attn_strides_t qs, const void* k
     f.B = B; f.H = H; f.Sq = Sq; f.D = D;
     f.n_qt = (int)((Sq + lsdit::kSkRows - 1) / lsdit::kSkRows);
     f.T = lsdit::fp8_key_tiles(Skv);
-    f.n_dp = p.n_dp; f.n_q = (int)n_qtiles(B, H, Sq); f.sk_wgs = p.sk_wgs;
+    f.n_dp = p.n_dp; f.n_q = (int)n_qtiles(B, H, Sq); f.sk_wgs = p.sk_wgs; f.sk_parts = p.parts;
     f.sk_o = a.sk_o; f.sk_lse = a.sk_lse;
     f.o = o; f.os = S(os); f.o_bf16 = o_dt == ATTN_BF16; f.lse = lse;
     return lsdit::launch_sk_fixup(f, s) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;

@@ -587,25 +587,40 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             g_first = 0;
             nkt = nkt_all;
         } else {
-            // the tail's runs in plain dispatch order: the XCDs take them round-robin, so the
-            // runs on one XCD are 8 apart, whose start keys differ by 8 U / P units, often a
-            // whole number of query tiles (the ring share) or half of one (the full
-            // sequence): they stream the same key tiles together and share them in the L2
-            // (remapped to consecutive runs, their starts spread over the whole key range)
+            // the tail's runs in plain order: the XCDs take them round-robin (or from their
+            // queues by b % 8), so the runs on one XCD are 8 apart.  Runs of equal unit ranges
+            // start 8 U / P units apart, often a whole number of query tiles (the ring share) or
+            // half of one (the full sequence): they stream the same key tiles together and
+            // share them in the L2 (remapped to consecutive runs, their starts spread over the
+            // whole key range).  Parts are numbered part-major, so an XCD's runs at one time are
+            // mostly the same part, the same key range, of different tail tiles.
             const int sk_w = bid - ar.n_dp;
-            const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
-            const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
-            // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1
-            const int64_t cut = (u0 / nkt_all + 1) * nkt_all;
-            const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
-            if (seg > 1 || s0 >= s1) {
-                seg = 0;
-                continue;
+            if (ar.sk_parts > 0) {
+                // part p = sk_w / n_tail of tail tile sk_w % n_tail: one segment
+                if (seg > 0) {
+                    seg = 0;
+                    continue;
+                }
+                const int n_tail = n_qtiles - ar.n_dp, p = sk_w / n_tail;
+                tile = ar.n_dp + sk_w % n_tail;
+                g_first = (int)((int64_t)nkt_all * p / ar.sk_parts);
+                nkt = (int)((int64_t)nkt_all * (p + 1) / ar.sk_parts) - g_first;
+                sk_slot_ = sk_w;
+            } else {
+                const int64_t U = (int64_t)(n_qtiles - ar.n_dp) * nkt_all;
+                const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
+                // segment 0 runs to the end of u0's query tile (or to u1), segment 1 from there to u1
+                const int64_t cut = (u0 / nkt_all + 1) * nkt_all;
+                const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
+                if (seg > 1 || s0 >= s1) {
+                    seg = 0;
+                    continue;
+                }
+                sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / nkt_all), ar.sk_wgs);
+                tile = ar.n_dp + (int)(s0 / nkt_all);
+                g_first = (int)(s0 % nkt_all);
+                nkt = (int)(s1 - s0);
             }
-            sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / nkt_all), ar.sk_wgs);
-            tile = ar.n_dp + (int)(s0 / nkt_all);
-            g_first = (int)(s0 % nkt_all);
-            nkt = (int)(s1 - s0);
         }
         // wave-uniform: the 64-bit divisions above run on the vector unit, and left there the
         // key loop's control flow derived from these would become per-lane
@@ -910,6 +925,10 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
     if (a.sk_wgs != 0) {
         // a stream-K tail: every run of its units must stay within two query tiles
         if (a.n_dp < 0 || a.n_dp >= n_q || a.sk_wgs <= n_q - a.n_dp || !a.sk_o || !a.sk_lse)
+            return hipErrorInvalidValue;
+        int64_t T = 0;
+        for (int c = 0; c < a.n_chunks && c < kMaxChunks; ++c) T += (a.chunk_len[c] + C::BK - 1) / C::BK;
+        if (a.sk_parts < 0 || (a.sk_parts > 0 && (a.sk_parts > T || (int64_t)a.sk_parts * (n_q - a.n_dp) != a.sk_wgs)))
             return hipErrorInvalidValue;
         n_tiles = (int64_t)a.n_dp + a.sk_wgs;
     }

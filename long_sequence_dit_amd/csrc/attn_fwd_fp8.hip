@@ -464,24 +464,39 @@ __global__ __launch_bounds__(NT, 1) void fwd_fp8_kernel(Fp8Args a, int n_qt, int
             g_first = 0;
             nkt = n_kt;
         } else {
-            // the tail's runs in plain dispatch order: the XCDs take them round-robin, so the
-            // runs on one XCD are 8 apart, whose start keys differ by 8 U / P units, often a
-            // whole number of query tiles (the ring share) or half of one (the full
-            // sequence): they stream the same key tiles together and share them in the L2
-            // (remapped to consecutive runs, their starts spread over the whole key range)
+            // the tail's runs in plain order: the XCDs take them round-robin (or from their
+            // queues by b % 8), so the runs on one XCD are 8 apart.  Runs of equal unit ranges
+            // start 8 U / P units apart, often a whole number of query tiles (the ring share) or
+            // half of one (the full sequence): they stream the same key tiles together and
+            // share them in the L2 (remapped to consecutive runs, their starts spread over the
+            // whole key range).  Parts are numbered part-major, so an XCD's runs at one time are
+            // mostly the same part, the same key range, of different tail tiles.
             const int sk_w = bid - ar.n_dp;
-            const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
-            const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
-            const int64_t cut = (u0 / n_kt + 1) * n_kt;
-            const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
-            if (seg > 1 || s0 >= s1) {
-                seg = 0;
-                continue;
+            if (ar.sk_parts > 0) {
+                // part p = sk_w / n_tail of tail tile sk_w % n_tail: one segment
+                if (seg > 0) {
+                    seg = 0;
+                    continue;
+                }
+                const int n_tail = n_q - ar.n_dp, p = sk_w / n_tail;
+                gidx = ar.n_dp + sk_w % n_tail;
+                g_first = (int)((int64_t)n_kt * p / ar.sk_parts);
+                nkt = (int)((int64_t)n_kt * (p + 1) / ar.sk_parts) - g_first;
+                sk_slot_ = sk_w;
+            } else {
+                const int64_t U = (int64_t)(n_q - ar.n_dp) * n_kt;
+                const int64_t u0 = sk_start(U, sk_w, ar.sk_wgs), u1 = sk_start(U, sk_w + 1, ar.sk_wgs);
+                const int64_t cut = (u0 / n_kt + 1) * n_kt;
+                const int64_t s0 = seg == 0 ? u0 : cut, s1 = seg == 0 ? (u1 < cut ? u1 : cut) : u1;
+                if (seg > 1 || s0 >= s1) {
+                    seg = 0;
+                    continue;
+                }
+                sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / n_kt), ar.sk_wgs);
+                gidx = ar.n_dp + (int)(s0 / n_kt);
+                g_first = (int)(s0 % n_kt);
+                nkt = (int)(s1 - s0);
             }
-            sk_slot_ = sk_slot(sk_w, seg, (int)(s0 / n_kt), ar.sk_wgs);
-            gidx = ar.n_dp + (int)(s0 / n_kt);
-            g_first = (int)(s0 % n_kt);
-            nkt = (int)(s1 - s0);
         }
         gidx = __builtin_amdgcn_readfirstlane(gidx);
         g_first = __builtin_amdgcn_readfirstlane(g_first);
@@ -740,6 +755,8 @@ hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream) {
     if (a.sk_wgs != 0) {
         // a stream-K tail: every run of its units must stay within two query tiles
         if (a.n_dp < 0 || a.n_dp >= n_q || a.sk_wgs <= n_q - a.n_dp || !a.sk_o || !a.sk_lse)
+            return hipErrorInvalidValue;
+        if (a.sk_parts < 0 || (a.sk_parts > 0 && (a.sk_parts > n_kt || (int64_t)a.sk_parts * (n_q - a.n_dp) != a.sk_wgs)))
             return hipErrorInvalidValue;
         blocks = (int64_t)a.n_dp + a.sk_wgs;
     }

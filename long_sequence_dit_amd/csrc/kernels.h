@@ -38,14 +38,18 @@ struct FwdArgs {
     // Balanced tail (bf16 and FP8 paths): sk_wgs > 0 makes n_items = n_dp + sk_wgs.  Items below
     // n_dp are whole query tiles (xcd_remap over the first n_dp) and write the final output.  The
     // other query tiles make U = (n_q - n_dp) * T units (query tile, key tile), T key tiles per
-    // query tile; item n_dp + w is the tail's run w, units [sk_start(U, w, sk_wgs),
-    // sk_start(U, w + 1, sk_wgs)): at most two query-tile segments, because sk_wgs > n_q - n_dp
-    // makes every run at most T long.  Each segment is written as an fp32 partial (normalised by
-    // its own row sum) with its natural-log LSE into slot sk_slot(...): row r of the query tile
+    // query tile; item n_dp + w is the tail's run w.  With sk_parts == 0 the runs are equal unit
+    // ranges: run w takes units [sk_start(U, w, sk_wgs), sk_start(U, w + 1, sk_wgs)), at most two
+    // query-tile segments because sk_wgs > n_q - n_dp makes every run at most T long, each
+    // written to slot sk_slot(...).  With sk_parts == r >= 2 (sk_wgs = r * n_tail, r <= T) every
+    // tail tile is cut into r parts: run w is key tiles [T p / r, T (p + 1) / r) of tail tile
+    // w % n_tail, p = w / n_tail, one segment, slot w.  Each segment is written as an fp32
+    // partial (normalised by its own row sum) with its natural-log LSE: row r of the query tile
     // at sk_o + slot*kSkRows*D + r*D and sk_lse + slot*kSkRows + r.  launch_sk_fixup then merges
     // the partials into the final output.
     int n_dp;
     int sk_wgs;          // runs of the tail; 0 = no tail
+    int sk_parts;        // 0: runs of equal unit ranges; r >= 2: r parts per tail tile
     float* sk_o;
     float* sk_lse;
     // Dispatch.  persist == 0: one workgroup per item.  persist > 0: a persistent
@@ -139,6 +143,7 @@ struct SkFixupArgs {
     int n_qt;            // query tiles per (b, h): ceil(Sq / kSkRows)
     int T;               // key tiles per query tile
     int n_dp, n_q, sk_wgs;
+    int sk_parts;        // as in FwdArgs
     const float* sk_o;
     const float* sk_lse;
     void* o;             // final output, strides os, bf16 or fp32
@@ -194,6 +199,7 @@ struct Fp8Args {
     // T = fp8_key_tiles(Skv))
     int n_dp;
     int sk_wgs;          // runs of the tail; 0 = no tail
+    int sk_parts;
     float* sk_o;
     float* sk_lse;
     int persist;

@@ -116,12 +116,35 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }
 
 // The balanced tail of the forward kernels (FwdArgs) left, for each query tile j of the tail,
-// fp32 partials over consecutive runs of its T key tiles, one per run whose unit range meets
-// [jT, (j+1)T).  The first of them is the last run starting at or before jT:
-// w = floor(((jT + 1) P - 1) / U) for P runs over U units (runs may be empty when U < P).  A run
-// that starts before jT continues into tile j as its second segment (slot P + j - 1, sk_slot);
-// the others start in tile j (slot w).  The runs merge by the LSE rule above; a tile's rows are
-// read and written once.
+// fp32 partials over consecutive runs of its T key tiles.  TailRuns lists their slots.
+//  * Runs of equal unit ranges (sk_parts == 0): one per run whose range meets [jT, (j+1)T).  The
+//    first is the last run starting at or before jT: w = floor(((jT + 1) P - 1) / U) for P runs
+//    over U units (runs may be empty when U < P).  A run that starts before jT continues into
+//    tile j as its second segment (slot P + j - 1, sk_slot); the others start in tile j (slot w).
+//  * r parts per tile (sk_parts == r): part p of tile j is run p * n_tail + j, in that slot.
+// The runs merge by the LSE rule above; a tile's rows are read and written once.
+struct TailRuns {
+    int j, P, parts, n_tail, w0;
+    int64_t U, t0, t1;
+    __device__ TailRuns(const SkFixupArgs& a, int j_) : j(j_), P(a.sk_wgs), parts(a.sk_parts) {
+        n_tail = a.n_q - a.n_dp;
+        U = (int64_t)n_tail * a.T;
+        t0 = (int64_t)j * a.T;
+        t1 = t0 + a.T;
+        w0 = parts > 0 ? 0 : (int)(((t0 + 1) * P - 1) / U);
+    }
+    // the i-th run's slot; -2: an empty run (skip it); -1: no more runs
+    __device__ int slot(int i) const {
+        if (parts > 0) return i < parts ? i * n_tail + j : -1;
+        const int w = w0 + i;
+        if (w >= P) return -1;
+        const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
+        if (u0 >= t1) return -1;
+        if (u1 == u0) return -2;
+        return sk_slot(w, u0 < t0 ? 1 : 0, j, P);
+    }
+};
+
 __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     const int lanes_per_row = a.D / 4;
     const int rows_per_block = kThreads / lanes_per_row;
@@ -132,10 +155,7 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     const int tile = a.n_dp + j;
     const int bh = tile / a.n_qt, s = (tile % a.n_qt) * kSkRows + r;
     if (s >= a.Sq) return;
-    const int P = a.sk_wgs;
-    const int64_t U = (int64_t)(a.n_q - a.n_dp) * a.T;
-    const int64_t t0 = (int64_t)j * a.T, t1 = t0 + a.T;
-    const int w0 = (int)(((t0 + 1) * P - 1) / U);
+    const TailRuns runs(a, j);
 
     // a running result over earlier keys, if given, is one more part (row bh*Sq + s of run_o)
     const int64_t orow = (int64_t)bh * a.Sq + s;
@@ -146,11 +166,10 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
         M = l_run;
         tot = 1.f;
     }
-    for (int w = w0; w < P; ++w) {
-        const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
-        if (u0 >= t1) break;
-        if (u1 == u0) continue;
-        const int slot = sk_slot(w, u0 < t0 ? 1 : 0, j, P);
+    for (int i = 0;; ++i) {
+        const int slot = runs.slot(i);
+        if (slot == -1) break;
+        if (slot < 0) continue;
         const float l = a.sk_lse[(int64_t)slot * kSkRows + r];
         nan |= l != l;
         if (l == -INFINITY || l != l) continue;
@@ -163,11 +182,11 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     if (M != -INFINITY) {
         const float L = M + logf(tot);
         if (l_run != -INFINITY) acc = expf(l_run - L) * *(const f32x4_t*)(a.run_o + orow * a.D + d);
-        for (int w = w0; w < P; ++w) {
-            const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
-            if (u0 >= t1) break;
-            if (u1 == u0) continue;
-            const int64_t row = (int64_t)sk_slot(w, u0 < t0 ? 1 : 0, j, P) * kSkRows + r;
+        for (int i = 0;; ++i) {
+            const int slot = runs.slot(i);
+            if (slot == -1) break;
+            if (slot < 0) continue;
+            const int64_t row = (int64_t)slot * kSkRows + r;
             const f32x4_t x = __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d));
             acc += expf(a.sk_lse[row] - L) * x;
         }
@@ -227,6 +246,8 @@ hipError_t launch_sk_fixup(const SkFixupArgs& a, hipStream_t stream) {
     const int n_tail = a.n_q - a.n_dp;
     if (n_tail <= 0) return hipSuccess;
     if ((a.D != 64 && a.D != 128) || a.sk_wgs <= 0 || a.T <= 0) return hipErrorInvalidValue;
+    if (a.sk_parts < 0 || (a.sk_parts > 0 && (a.sk_parts > a.T || (int64_t)a.sk_parts * n_tail != a.sk_wgs)))
+        return hipErrorInvalidValue;
     const int blocks_per_tile = kSkRows / (kThreads / (a.D / 4));
     const int64_t blocks = (int64_t)n_tail * blocks_per_tile;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -214,9 +214,9 @@ def test_fp8_argument_errors(attn):
     # 16 heads x 173 query tiles against 690 key tiles leave 208 tiles in the last round of 256 CUs
     # (the CPU build assumes 256): room for the balanced tail after V^T; 16 x 16 tiles fill it
     vt = 16 * 690 * 8192
-    # a persistent launch (2768 tiles x 690 key tiles): the work queues, then a slot per run (2 per
-    # CU: 143,520 units, each run at least 256 FP8 key tiles) and per tail tile
-    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + WQ + _tail_room(2 * 256 + 208)
+    # a persistent launch (2768 tiles x 690 key tiles): the work queues, then a slot per run: each
+    # of the 208 tail tiles cut into 2 parts (parts of at least 256 FP8 key tiles)
+    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + WQ + _tail_room(2 * 208)
     assert lib.attn_fp8_workspace_size(1, 16, 4096, 44160, 128) == vt
 
     def f(q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=need, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1, dq=1.0, dk=1.0,

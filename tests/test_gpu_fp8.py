@@ -176,24 +176,24 @@ def test_fp8_balanced_tail():
     check_fp8(o, l, inp, 1 / math.sqrt(128), what="fp8 balanced tail")
 
 
-@pytest.mark.parametrize("runs", [1, 4])
-def test_fp8_persistent_dispatch(runs, monkeypatch):
+@pytest.mark.parametrize("tail", ["ranges", "5"])
+def test_fp8_persistent_dispatch(tail, monkeypatch):
     """300 query tiles (20 heads x 15) against 79 key tiles, the persistent launch forced on (the
     library's debug switch; at full size the 44,160-key shapes choose it themselves): with one
-    tail run per CU bitwise equal to one workgroup per item, with four (1,024 runs of 3-4 key
-    tiles, many crossing query tiles) within the bound on sampled rows of every head."""
+    tail run of equal units per CU bitwise equal to one workgroup per item; with the 44 tail
+    tiles cut into 5 parts within the bound on sampled rows of every head."""
     B, H, Sq, Skv = 1, 20, 3600, 5000
     inp = _quantized(B, H, Sq, Skv, seed=12)
-    print("fp8 persistent, %d tail runs per CU" % runs, flush=True)
-    monkeypatch.setenv("LSDIT_DEBUG_TAIL_RUNS", str(runs))
+    print("fp8 persistent, tail %s" % tail, flush=True)
+    monkeypatch.setenv("LSDIT_DEBUG_TAIL", tail)
     monkeypatch.setenv("LSDIT_DEBUG_PERSIST", "1")
     o, l = _run(inp, 0.1, torch.float32)
-    if runs == 1:
+    if tail == "ranges":
         monkeypatch.setenv("LSDIT_DEBUG_PERSIST", "0")
         o_s, l_s = _run(inp, 0.1, torch.float32)
         assert torch.equal(o, o_s) and torch.equal(l, l_s)
     rows = sorted({0, 255, 256, 3583, 3584, 3599} | set(range(0, Sq, 211)))
-    check_fp8(o, l, inp, 0.1, rows=rows, what="fp8 persistent runs=%d" % runs)
+    check_fp8(o, l, inp, 0.1, rows=rows, what="fp8 persistent tail %s" % tail)
 
 
 FULL = ["image_dit", "ring_share_r0", "ulysses_share", "full_sequence"]

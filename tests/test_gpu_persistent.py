@@ -4,10 +4,10 @@ then the balanced tail's runs) from per-XCD work queues.
 Which workgroup takes an item must not change any result: every item writes its own rows or
 partial slots.  Launches of several rounds with enough work per CU run persistent by themselves;
 the library's debug switches force it (LSDIT_DEBUG_PERSIST=1) or forbid it (=0) and fix the
-tail's runs per CU (LSDIT_DEBUG_TAIL_RUNS), so that these checks run at sizes the oracle finishes
-in seconds: bitwise against the one-workgroup-per-item dispatch with the same tail, bitwise
-repeatable, and with up to four runs per CU (runs of 3-4 key tiles, many crossing query tiles)
-against the oracle.
+tail (LSDIT_DEBUG_TAIL: "ranges" for one run of equal units per CU, as a launch of one workgroup
+per item has; r for r parts per tail tile), so that these checks run at sizes the oracle
+finishes in seconds: bitwise against the one-workgroup-per-item dispatch with the same tail,
+bitwise repeatable, and with the tail tiles cut into parts against the oracle.
 """
 import math
 
@@ -39,12 +39,12 @@ def _inputs(B, H, Sq, Skv, D, seed):
                  for i, S in enumerate((Sq, Skv, Skv)))
 
 
-def _run(qd, kd, vd, lens, order, mode, monkeypatch, persist, runs=None, out_dtype=torch.float32):
+def _run(qd, kd, vd, lens, order, mode, monkeypatch, persist, tail=None, out_dtype=torch.float32):
     monkeypatch.setenv("LSDIT_DEBUG_PERSIST", persist)
-    if runs is None:
-        monkeypatch.delenv("LSDIT_DEBUG_TAIL_RUNS", raising=False)
+    if tail is None:
+        monkeypatch.delenv("LSDIT_DEBUG_TAIL", raising=False)
     else:
-        monkeypatch.setenv("LSDIT_DEBUG_TAIL_RUNS", str(runs))
+        monkeypatch.setenv("LSDIT_DEBUG_TAIL", str(tail))
     o, l = A().shard_fwd(qd, kd, vd, lens, order, mode=mode, out_dtype=out_dtype)
     torch.cuda.synchronize()
     return o, l
@@ -65,28 +65,30 @@ def test_persistent_dispatch_matches_one_workgroup_per_item(shape, mode, monkeyp
     lens, order = (Skv // 3, Skv - Skv // 3), (1, 0)
     print("persistent vs static: shape %s mode %s" % (shape, mode), flush=True)
     o_s, l_s = _run(qd, kd, vd, lens, order, mode, monkeypatch, "0")
-    o_p, l_p = _run(qd, kd, vd, lens, order, mode, monkeypatch, "1", runs=1)
+    o_p, l_p = _run(qd, kd, vd, lens, order, mode, monkeypatch, "1", tail="ranges")
     assert torch.equal(o_s, o_p) and torch.equal(l_s, l_p)
 
 
-@pytest.mark.parametrize("runs", [2, 4])
-def test_persistent_tail_runs_match_the_oracle(runs, monkeypatch):
-    """Four runs per CU over the 44 tail tiles' 3476 units: 1024 runs of 3-4 key tiles, about 23
-    partials per tail row.  Rows of whole tiles, of tail tiles (first, crossing, last) and of the
-    ragged last tile of a head match the oracle, and the result is bitwise repeatable."""
+@pytest.mark.parametrize("parts", [2, 5, 23])
+def test_persistent_tail_parts_match_the_oracle(parts, monkeypatch):
+    """The 44 tail tiles against 79 key tiles cut into 2, 5 or 23 parts (39-40 down to 3-4 key
+    tiles each, 88 to 1012 runs: 23 parts is the most the workspace's tail room holds, 4 runs per
+    CU plus one slot per tail tile), `parts` partials per tail row.  Rows of whole tiles, of tail
+    tiles and of the ragged last tile of a head match the oracle, and the result is bitwise
+    repeatable."""
     B, H, Sq, Skv, D = 1, 20, 3600, 5000, 128
     q, k, v = _inputs(B, H, Sq, Skv, D, seed=43)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     lens, order = (2000, 3000), (1, 0)
-    print("persistent, %d tail runs per CU" % runs, flush=True)
-    o, l = _run(qd, kd, vd, lens, order, "fused", monkeypatch, "1", runs=runs, out_dtype=torch.bfloat16)
+    print("persistent, tail tiles in %d parts" % parts, flush=True)
+    o, l = _run(qd, kd, vd, lens, order, "fused", monkeypatch, "1", tail=parts, out_dtype=torch.bfloat16)
     rows = sorted({0, 255, 256, 3583, 3584, 3599} | set(range(0, Sq, 89)))
     for h in (0, 17, 19):  # whole tiles only; tail from tile 256 (head 17, tile 1); tail only
         o_ref, l_ref = oracle.attention(q[:, h:h + 1, rows], k[:, h:h + 1], v[:, h:h + 1], 1 / math.sqrt(D))
         assert_parity(o[:, h:h + 1, rows], l[:, h:h + 1, rows], o_ref, l_ref,
-                      what="persistent runs=%d head %d" % (runs, h))
+                      what="persistent parts=%d head %d" % (parts, h))
     for _ in range(3):
-        o2, l2 = _run(qd, kd, vd, lens, order, "fused", monkeypatch, "1", runs=runs, out_dtype=torch.bfloat16)
+        o2, l2 = _run(qd, kd, vd, lens, order, "fused", monkeypatch, "1", tail=parts, out_dtype=torch.bfloat16)
         assert torch.equal(o, o2) and torch.equal(l, l2)
 
 
@@ -97,5 +99,5 @@ def test_persistent_one_round_runs_one_workgroup_per_item(monkeypatch):
     q, k, v = _inputs(B, H, Sq, Skv, D, seed=45)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
-    o, l = _run(qd, kd, vd, (Skv,), None, "fused", monkeypatch, "1", runs=4, out_dtype=torch.bfloat16)
+    o, l = _run(qd, kd, vd, (Skv,), None, "fused", monkeypatch, "1", tail=5, out_dtype=torch.bfloat16)
     assert_parity(o, l, o_ref, l_ref, what="one round, persistence asked")

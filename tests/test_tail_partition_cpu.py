@@ -12,6 +12,10 @@ segment, no two segments share a slot, and the fix-up finds exactly the runs tha
 tile, with the slots the kernel wrote.  P is one run per CU, or up to four when the launch is
 persistent.
 
+A persistent launch cuts every tail tile into r equal parts instead (part p of tile j is run
+p * n_tail + j, key tiles [T p / r, T (p + 1) / r), slot p * n_tail + j): checked likewise, for
+the r the library's rule picks and for forced ones.
+
 A persistent launch of G workgroups gives workgroup g item g first; the other items are dealt
 by b % 8 over 8 queues of whole query tiles and 8 of tail runs, and a workgroup takes from its
 own XCD's whole-tile queue, the other whole-tile queues, then the tail queues.  Simulated with
@@ -99,6 +103,61 @@ def test_first_workgroup_formula_is_the_last_start_at_or_before():
         for x in range(U):
             w = ((x + 1) * P - 1) // U
             assert sk_start(U, w, P) <= x and (w + 1 == P or sk_start(U, w + 1, P) > x)
+
+
+def part_segments(T, r, n_tail, w):
+    """(tile, first key tile, key tiles, slot) of run w of the r-part tail, as the kernel's."""
+    p, j = w // n_tail, w % n_tail
+    g0, g1 = T * p // r, T * (p + 1) // r
+    return [(j, g0, g1 - g0, w)]
+
+
+def part_fixup_slots(r, n_tail, j):
+    return [p * n_tail + j for p in range(r)]
+
+
+def library_parts(n_tail, T, cus=256, min_run=128, most_per_cu=4):
+    """The library's choice of r for a persistent launch (0: runs of equal units)."""
+    most = (most_per_cu * cus + n_tail - 1) // n_tail
+    r = min(T // min_run, most)
+    if r * n_tail < cus:
+        r = 0
+    return r if 2 <= r <= T else 0
+
+
+PART_CASES = [(208, 690, None), (96, 690, None), (180, 690, None), (208, 690, 2), (44, 79, 5), (3, 79, 79),
+              (255, 2000, None), (1, 2000, None), (7, 16, 16)]
+PART_CASES += [(rng.randint(1, 255), rng.randint(2, 3000), None) for _ in range(20)]
+
+
+@pytest.mark.parametrize("n_tail,T,forced", PART_CASES)
+def test_parts_every_unit_once_and_fixup_finds_them(n_tail, T, forced):
+    r = forced or library_parts(n_tail, T)
+    if r == 0:
+        assert n_tail * min(T // 128, (1024 + n_tail - 1) // n_tail) < 256 or T // 128 < 2
+        return
+    assert 2 <= r <= T and r * n_tail <= 4 * 256 + n_tail  # fits the workspace's tail room
+    covered = [0] * (n_tail * T)
+    by_tile = {}
+    slots = []
+    for w in range(r * n_tail):
+        for tile, g0, n, slot in part_segments(T, r, n_tail, w):
+            assert n >= 1 and g0 + n <= T
+            for u in range(tile * T + g0, tile * T + g0 + n):
+                covered[u] += 1
+            by_tile.setdefault(tile, []).append(slot)
+            slots.append(slot)
+    assert all(c == 1 for c in covered)
+    assert sorted(slots) == list(range(r * n_tail))
+    for j in range(n_tail):
+        assert sorted(part_fixup_slots(r, n_tail, j)) == sorted(by_tile[j])
+
+
+def test_library_parts_at_the_workloads():
+    # full sequence, ring share, Ulysses share (bf16); the FP8 kernel's parts are twice as long
+    assert library_parts(208, 690) == 5 and library_parts(96, 690) == 5 and library_parts(180, 690) == 5
+    assert library_parts(208, 690, min_run=256) == 2 and library_parts(180, 690, min_run=256) == 2
+    assert library_parts(208, 87) == 0  # a ring chunk's launch: runs of equal units
 
 
 def wq_next(counters, xcd, G, n_whole, n_items, empty):
