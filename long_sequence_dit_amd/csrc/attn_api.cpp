@@ -132,16 +132,19 @@ int device_cus() {
 // time, so its fixed costs weigh about twice as many tiles.
 //  * A launch of one workgroup per item cuts the tail into one run of equal units per CU: the
 //    hardware deals the runs out as CUs come free, and equal runs end together.
-//  * A persistent launch (FwdArgs::persist) cuts every tail tile into r equal parts instead, r
-//    as large as runs of at least min_run key tiles and at most kSkMaxRunsPerCu runs per CU
-//    allow, so that its queues balance the end to a fraction of a query tile, given at least one
-//    run per CU (else one run of equal units per CU, as above).  A run's fixed costs (prologue,
-//    epilogue, fp32 partial, the queue) come to about 9 us: at 65 key tiles per run (the ring
-//    share, runs of equal units cut 4 ways) they outweighed the balance gained on a box whose
-//    XCDs were close (2.5% slower), at 140 (the full sequence) they did not (1% faster); on the
-//    slowest boxes seen the finer tail gained 4% at either.  Parts, unlike runs of equal units,
-//    never cross a tile boundary, and the queues hand them out part-major, so that an XCD's runs
-//    at one time read the same key range.
+//  * A persistent launch (FwdArgs::persist) cuts every tail tile into r equal parts instead, so
+//    that its queues balance the end to a fraction of a query tile.  Parts, unlike runs of equal
+//    units, never cross a tile boundary, and the queues hand them out part-major, so that an
+//    XCD's runs at one time read the same key range.  r is at most what parts of min_run key
+//    tiles and kSkMaxRunsPerCu runs per CU allow: a run's fixed costs (prologue, epilogue, fp32
+//    partial, the queue) come to about 9 us, and at 65 key tiles per run they outweighed the
+//    balance gained on a box whose XCDs were close.  Among those r it takes the one whose
+//    n = r * n_tail parts fill the CUs' last round of parts best (the least ceil(n/cus) /
+//    (n/cus) - 1; a larger r unless a smaller one is better by 0.02): the tail's parts all start
+//    at about the same time, so a last round that is part-full costs nearly a whole part (the
+//    ring share: 1.65 ms at 5 parts, 1.70 at 4 and 1.79-1.81 at 3, whose 288 parts leave 224
+//    CUs a second round).  Above 0.3, and with fewer parts than CUs, one run of equal units
+//    per CU balances better.
 // The persistent launch itself pays off from about kPersistMinTiles key tiles per CU (its
 // queues cost a few microseconds per item): the XCDs' clocks differ by up to ~8%, and a static
 // grid ends with the slowest XCD (44,160-key shares: 4-7% faster on the slowest boxes, 1% on the
@@ -169,8 +172,18 @@ SkPlan sk_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, bool persist
     p.sk_wgs = (int)(U < cus ? U : cus);
     if (persist) {
         const int64_t most = ((int64_t)kSkMaxRunsPerCu * cus + rem - 1) / rem;
-        int64_t r = T / min_run < most ? T / min_run : most;
-        if (r * rem < cus) r = 0;  // fewer parts than CUs: equal units balance better
+        const int64_t r_max = T / min_run < most ? T / min_run : most;
+        int64_t r = 0;
+        double best = 0.3;  // the most a last round of parts may leave idle, relative
+        for (int64_t c = r_max; c >= 2; --c) {
+            const double per = (double)(c * rem) / cus;
+            if (per < 1.0) break;  // fewer parts than CUs
+            const double idle = (double)((c * rem + cus - 1) / cus) / per - 1.0;
+            if (r == 0 ? idle <= best : idle < best - 0.02) {
+                r = c;
+                best = idle;
+            }
+        }
         const int dt = debug_tail();
         if (dt >= 0) r = dt;
         if (r >= 2 && r <= T) {
@@ -204,8 +217,8 @@ size_t tail_room(int64_t n_q, int cus, int D) {
 
 // The persistent launch and its tail for a launch of n_q query tiles against T key tiles: bf16
 // (weight 1) or FP8, whose tiles take about half the time (weight 2: twice the tiles per CU
-// before the queues pay, twice the key tiles per run).  persist_ok: the caller has room for the
-// work queues.
+// before the queues pay, 1.5 times the key tiles per part).  persist_ok: the caller has room for
+// the work queues.
 struct LaunchPlan {
     bool persist = false;
     SkPlan sk;
@@ -214,7 +227,8 @@ LaunchPlan launch_plan(int64_t n_q, int64_t T, int cus, int64_t min_saving, int6
     LaunchPlan lp;
     lp.persist = persist_ok && n_q > cus && n_q * T >= kPersistMinTiles * weight * cus;
     if (debug_persist() >= 0) lp.persist = persist_ok && n_q > cus && debug_persist() == 1;
-    lp.sk = sk_plan(n_q, T, cus, min_saving, lp.persist, kSkMinRunTiles * weight);
+    // FP8 parts of 256 key tiles ran 0.8% slower than parts of 172-230 at the full sequence
+    lp.sk = sk_plan(n_q, T, cus, min_saving, lp.persist, weight == 1 ? kSkMinRunTiles : kSkMinRunTiles * 3 / 2);
     return lp;
 }
 

@@ -166,29 +166,57 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
         M = l_run;
         tot = 1.f;
     }
-    for (int i = 0;; ++i) {
-        const int slot = runs.slot(i);
-        if (slot == -1) break;
-        if (slot < 0) continue;
-        const float l = a.sk_lse[(int64_t)slot * kSkRows + r];
-        nan |= l != l;
-        if (l == -INFINITY || l != l) continue;
-        const float m_new = fmaxf(M, l);
-        tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
-        M = m_new;
+    // the runs' slots four at a time, so that their loads are in flight together (a slot of -1
+    // ends the list, and every later one is -1 too; -2, an empty run, is skipped)
+    constexpr int kB = 4;
+    for (int i = 0;; i += kB) {
+        int sl[kB];
+        float lb[kB];
+        bool end = false;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            sl[u] = end ? -1 : runs.slot(i + u);
+            end |= sl[u] == -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) lb[u] = sl[u] >= 0 ? a.sk_lse[(int64_t)sl[u] * kSkRows + r] : -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const float l = lb[u];
+            nan |= l != l;
+            if (l == -INFINITY || l != l) continue;
+            const float m_new = fmaxf(M, l);
+            tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
+            M = m_new;
+        }
+        if (end) break;
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lse_out = -INFINITY;
     if (M != -INFINITY) {
         const float L = M + logf(tot);
         if (l_run != -INFINITY) acc = expf(l_run - L) * *(const f32x4_t*)(a.run_o + orow * a.D + d);
-        for (int i = 0;; ++i) {
-            const int slot = runs.slot(i);
-            if (slot == -1) break;
-            if (slot < 0) continue;
-            const int64_t row = (int64_t)slot * kSkRows + r;
-            const f32x4_t x = __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d));
-            acc += expf(a.sk_lse[row] - L) * x;
+        for (int i = 0;; i += kB) {
+            int sl[kB];
+            f32x4_t x[kB];
+            float wl[kB];
+            bool end = false;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                sl[u] = end ? -1 : runs.slot(i + u);
+                end |= sl[u] == -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                const int64_t row = (int64_t)(sl[u] >= 0 ? sl[u] : 0) * kSkRows + r;
+                x[u] = sl[u] >= 0 ? __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d))
+                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                wl[u] = sl[u] >= 0 ? a.sk_lse[row] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (sl[u] >= 0) acc += expf(wl[u] - L) * x[u];
+            if (end) break;
         }
         lse_out = L;
     }

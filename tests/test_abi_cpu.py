@@ -215,8 +215,8 @@ def test_fp8_argument_errors(attn):
     # (the CPU build assumes 256): room for the balanced tail after V^T; 16 x 16 tiles fill it
     vt = 16 * 690 * 8192
     # a persistent launch (2768 tiles x 690 key tiles): the work queues, then a slot per run: each
-    # of the 208 tail tiles cut into 2 parts (parts of at least 256 FP8 key tiles)
-    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + WQ + _tail_room(2 * 208)
+    # of the 208 tail tiles cut into 3 parts (parts of at least 192 FP8 key tiles)
+    assert lib.attn_fp8_workspace_size(1, 16, 44160, 44160, 128) == vt + WQ + _tail_room(3 * 208)
     assert lib.attn_fp8_workspace_size(1, 16, 4096, 44160, 128) == vt
 
     def f(q=P, k=P, v=P, o=P, lse=P, ws=P, ws_bytes=need, B=1, H=2, Sq=10, Skv=20, D=128, scale=0.1, dq=1.0, dk=1.0,

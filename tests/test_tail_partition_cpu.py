@@ -117,12 +117,20 @@ def part_fixup_slots(r, n_tail, j):
 
 
 def library_parts(n_tail, T, cus=256, min_run=128, most_per_cu=4):
-    """The library's choice of r for a persistent launch (0: runs of equal units)."""
+    """The library's choice of r for a persistent launch (0: runs of equal units): the r <= r_max
+    whose parts leave the least of their last round idle (a larger r unless a smaller one is
+    better by 0.02), none above 0.3 or with fewer parts than CUs."""
     most = (most_per_cu * cus + n_tail - 1) // n_tail
-    r = min(T // min_run, most)
-    if r * n_tail < cus:
-        r = 0
-    return r if 2 <= r <= T else 0
+    r_max = min(T // min_run, most)
+    r, best = 0, 0.3
+    for c in range(r_max, 1, -1):
+        per = c * n_tail / cus
+        if per < 1.0:
+            break
+        idle = -(-(c * n_tail) // cus) / per - 1.0
+        if (idle <= best) if r == 0 else (idle < best - 0.02):
+            r, best = c, idle
+    return r
 
 
 PART_CASES = [(208, 690, None), (96, 690, None), (180, 690, None), (208, 690, 2), (44, 79, 5), (3, 79, 79),
@@ -134,7 +142,6 @@ PART_CASES += [(rng.randint(1, 255), rng.randint(2, 3000), None) for _ in range(
 def test_parts_every_unit_once_and_fixup_finds_them(n_tail, T, forced):
     r = forced or library_parts(n_tail, T)
     if r == 0:
-        assert n_tail * min(T // 128, (1024 + n_tail - 1) // n_tail) < 256 or T // 128 < 2
         return
     assert 2 <= r <= T and r * n_tail <= 4 * 256 + n_tail  # fits the workspace's tail room
     covered = [0] * (n_tail * T)
@@ -154,10 +161,14 @@ def test_parts_every_unit_once_and_fixup_finds_them(n_tail, T, forced):
 
 
 def test_library_parts_at_the_workloads():
-    # full sequence, ring share, Ulysses share (bf16); the FP8 kernel's parts are twice as long
-    assert library_parts(208, 690) == 5 and library_parts(96, 690) == 5 and library_parts(180, 690) == 5
-    assert library_parts(208, 690, min_run=256) == 2 and library_parts(180, 690, min_run=256) == 2
+    # full sequence, ring share, Ulysses share (bf16): 1040 parts (4.06 per CU), 480 (1.88), 720
+    # (2.81; 5 parts would make 3.52); the FP8 kernel's parts are at least 192 key tiles: 624 at
+    # the full sequence, none at the Ulysses share (2 or 3 parts per tile leave 42% of the last
+    # round idle)
+    assert library_parts(208, 690) == 5 and library_parts(96, 690) == 5 and library_parts(180, 690) == 4
+    assert library_parts(208, 690, min_run=192) == 3 and library_parts(180, 690, min_run=192) == 0
     assert library_parts(208, 87) == 0  # a ring chunk's launch: runs of equal units
+    assert library_parts(96, 690, min_run=170) == 0  # 4 parts: 1.5 per CU, 3 parts: 1.125
 
 
 def wq_next(counters, xcd, G, n_whole, n_items, empty):
