@@ -124,24 +124,35 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 //  * r parts per tile (sk_parts == r): part p of tile j is run p * n_tail + j, in that slot.
 // The runs merge by the LSE rule above; a tile's rows are read and written once.
 struct TailRuns {
-    int j, P, parts, n_tail, w0;
-    int64_t U, t0, t1;
-    __device__ TailRuns(const SkFixupArgs& a, int j_) : j(j_), P(a.sk_wgs), parts(a.sk_parts) {
+    int j, P, parts, n_tail, i;
+    // runs of equal units: run w starts at unit b, U w = b P + rm; U = q P + ru
+    int64_t t0, t1, q, ru, w, b, rm;
+    __device__ TailRuns(const SkFixupArgs& a, int j_) : j(j_), P(a.sk_wgs), parts(a.sk_parts), i(0) {
         n_tail = a.n_q - a.n_dp;
-        U = (int64_t)n_tail * a.T;
+        const int64_t U = (int64_t)n_tail * a.T;
         t0 = (int64_t)j * a.T;
         t1 = t0 + a.T;
-        w0 = parts > 0 ? 0 : (int)(((t0 + 1) * P - 1) / U);
+        w = parts > 0 ? 0 : ((t0 + 1) * P - 1) / U;
+        q = U / P;
+        ru = U - q * P;
+        b = U * w / P;
+        rm = U * w - b * P;
     }
-    // the i-th run's slot; -2: an empty run (skip it); -1: no more runs
-    __device__ int slot(int i) const {
-        if (parts > 0) return i < parts ? i * n_tail + j : -1;
-        const int w = w0 + i;
-        if (w >= P) return -1;
-        const int64_t u0 = sk_start(U, w, P), u1 = sk_start(U, w + 1, P);
-        if (u0 >= t1) return -1;
-        if (u1 == u0) return -2;
-        return sk_slot(w, u0 < t0 ? 1 : 0, j, P);
+    // the next run's slot; -2: an empty run (skip it); -1: no more runs.  Runs of equal units
+    // step from one boundary floor(U w / P) to the next without dividing.
+    __device__ int next() {
+        if (parts > 0) return i < parts ? (i++) * n_tail + j : -1;
+        if (w >= P || b >= t1) return -1;
+        int64_t b2 = b + q, rm2 = rm + ru;
+        if (rm2 >= P) {
+            rm2 -= P;
+            b2 += 1;
+        }
+        const int slot = b2 == b ? -2 : sk_slot((int)w, b < t0 ? 1 : 0, j, P);
+        w += 1;
+        b = b2;
+        rm = rm2;
+        return slot;
     }
 };
 
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
     const int tile = a.n_dp + j;
     const int bh = tile / a.n_qt, s = (tile % a.n_qt) * kSkRows + r;
     if (s >= a.Sq) return;
-    const TailRuns runs(a, j);
+    TailRuns runs(a, j);
 
     // a running result over earlier keys, if given, is one more part (row bh*Sq + s of run_o)
     const int64_t orow = (int64_t)bh * a.Sq + s;
@@ -166,57 +177,91 @@ __global__ __launch_bounds__(kThreads) void sk_fixup_kernel(SkFixupArgs a) {
         M = l_run;
         tot = 1.f;
     }
-    // the runs' slots four at a time, so that their loads are in flight together (a slot of -1
-    // ends the list, and every later one is -1 too; -2, an empty run, is skipped)
-    constexpr int kB = 4;
-    for (int i = 0;; i += kB) {
-        int sl[kB];
-        float lb[kB];
-        bool end = false;
+    // The first kH runs' partial rows and LSEs are loaded at once and held in registers (a tile
+    // has r parts, or about P / n_tail + 1 runs of equal units: rarely more), with the running
+    // result's row, so that one round trip to memory covers them; runs past those (a slot of -1
+    // ends the list, and every later one is -1 too; -2, an empty run, is skipped) follow four
+    // at a time, in two passes.  Either way the parts combine in run order.
+    constexpr int kH = 8, kB = 4;
+    int sh[kH];
+    bool end = false;
 #pragma unroll
-        for (int u = 0; u < kB; ++u) {
-            sl[u] = end ? -1 : runs.slot(i + u);
-            end |= sl[u] == -1;
+    for (int u = 0; u < kH; ++u) {
+        sh[u] = end ? -1 : runs.next();
+        end |= sh[u] == -1;
+    }
+    const bool more = !end;
+    const TailRuns rest = runs;  // positioned after the held runs
+    f32x4_t xh[kH];
+    float lh[kH];
+    const f32x4_t x_run = l_run != -INFINITY && !nan ? *(const f32x4_t*)(a.run_o + orow * a.D + d)
+                                                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kH; ++u) {
+        const int64_t row = (int64_t)(sh[u] >= 0 ? sh[u] : 0) * kSkRows + r;
+        xh[u] = sh[u] >= 0 ? __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d))
+                           : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lh[u] = sh[u] >= 0 ? a.sk_lse[row] : -INFINITY;
+    }
+    auto fold = [&](float l) {
+        nan |= l != l;
+        if (l == -INFINITY || l != l) return;
+        const float m_new = fmaxf(M, l);
+        tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
+        M = m_new;
+    };
+#pragma unroll
+    for (int u = 0; u < kH; ++u) fold(lh[u]);
+    if (more) {
+        TailRuns it = rest;
+        for (;;) {
+            int sl[kB];
+            float lb[kB];
+            bool e = false;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                sl[u] = e ? -1 : it.next();
+                e |= sl[u] == -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kB; ++u) lb[u] = sl[u] >= 0 ? a.sk_lse[(int64_t)sl[u] * kSkRows + r] : -INFINITY;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) fold(lb[u]);
+            if (e) break;
         }
-#pragma unroll
-        for (int u = 0; u < kB; ++u) lb[u] = sl[u] >= 0 ? a.sk_lse[(int64_t)sl[u] * kSkRows + r] : -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-            const float l = lb[u];
-            nan |= l != l;
-            if (l == -INFINITY || l != l) continue;
-            const float m_new = fmaxf(M, l);
-            tot = (M == -INFINITY ? 0.f : tot * expf(M - m_new)) + expf(l - m_new);
-            M = m_new;
-        }
-        if (end) break;
     }
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lse_out = -INFINITY;
     if (M != -INFINITY) {
         const float L = M + logf(tot);
-        if (l_run != -INFINITY) acc = expf(l_run - L) * *(const f32x4_t*)(a.run_o + orow * a.D + d);
-        for (int i = 0;; i += kB) {
-            int sl[kB];
-            f32x4_t x[kB];
-            float wl[kB];
-            bool end = false;
+        if (l_run != -INFINITY) acc = expf(l_run - L) * x_run;
 #pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                sl[u] = end ? -1 : runs.slot(i + u);
-                end |= sl[u] == -1;
+        for (int u = 0; u < kH; ++u)
+            if (sh[u] >= 0) acc += expf(lh[u] - L) * xh[u];
+        if (more) {
+            TailRuns it = rest;
+            for (;;) {
+                int sl[kB];
+                f32x4_t x[kB];
+                float wl[kB];
+                bool e = false;
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    sl[u] = e ? -1 : it.next();
+                    e |= sl[u] == -1;
+                }
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                    const int64_t row = (int64_t)(sl[u] >= 0 ? sl[u] : 0) * kSkRows + r;
+                    x[u] = sl[u] >= 0 ? __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d))
+                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    wl[u] = sl[u] >= 0 ? a.sk_lse[row] : -INFINITY;
+                }
+#pragma unroll
+                for (int u = 0; u < kB; ++u)
+                    if (sl[u] >= 0) acc += expf(wl[u] - L) * x[u];
+                if (e) break;
             }
-#pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                const int64_t row = (int64_t)(sl[u] >= 0 ? sl[u] : 0) * kSkRows + r;
-                x[u] = sl[u] >= 0 ? __builtin_nontemporal_load((const f32x4_t*)(a.sk_o + row * a.D + d))
-                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
-                wl[u] = sl[u] >= 0 ? a.sk_lse[row] : -INFINITY;
-            }
-#pragma unroll
-            for (int u = 0; u < kB; ++u)
-                if (sl[u] >= 0) acc += expf(wl[u] - L) * x[u];
-            if (end) break;
         }
         lse_out = L;
     }
