@@ -11,6 +11,7 @@ bitwise repeatable, and with the tail tiles cut into parts against the oracle.
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -101,3 +102,35 @@ def test_persistent_one_round_runs_one_workgroup_per_item(monkeypatch):
     o_ref, l_ref = oracle.attention(q, k, v, 1 / math.sqrt(D))
     o, l = _run(qd, kd, vd, (Skv,), None, "fused", monkeypatch, "1", tail=5, out_dtype=torch.bfloat16)
     assert_parity(o, l, o_ref, l_ref, what="one round, persistence asked")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_persistent_batches_strided_views_and_d64(D, out_dtype, monkeypatch):
+    """Two batches with [B,S,H,D] storage for Q, K, V and O, 2 x 11 heads x 12 query tiles = 264
+    (256 whole, 8 in the tail) against 5000 keys in two chunks, persistent, the tail tiles cut
+    into 7 parts: every element against the oracle, and bitwise against one workgroup per item
+    with one run of equal units per CU."""
+    B, Sq, Skv, H = 2, 3000, 5000, 11
+    rng = np.random.default_rng(7)
+    qb, kb, vb = (synth.f32_to_bf16_bits(rng.standard_normal((B, S, H, D)).astype(np.float32))
+                  for S in (Sq, Skv, Skv))
+    qd, kd, vd = (to_device(x).permute(0, 2, 1, 3) for x in (qb, kb, vb))
+    qh, kh, vh = (np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (qb, kb, vb))
+    o_ref, l_ref = oracle.attention(qh, kh, vh, 1 / math.sqrt(D))
+    print("persistent B=2 strided D=%d out %s" % (D, out_dtype), flush=True)
+
+    def run(persist, tail):
+        monkeypatch.setenv("LSDIT_DEBUG_PERSIST", persist)
+        monkeypatch.setenv("LSDIT_DEBUG_TAIL", tail)
+        out = torch.empty((B, Sq, H, D), dtype=out_dtype, device="cuda").permute(0, 2, 1, 3)
+        o, l = A().shard_fwd(qd, kd, vd, (1700, 3300), (1, 0), mode="fused", out=out)
+        torch.cuda.synchronize()
+        assert o.data_ptr() == out.data_ptr()
+        return o, l
+
+    o, l = run("1", "7")
+    assert_parity(o, l, o_ref, l_ref, what="persistent, 7 parts, B=2, strided, D=%d" % D)
+    o_p, l_p = run("1", "ranges")
+    o_s, l_s = run("0", "ranges")
+    assert torch.equal(o_p, o_s) and torch.equal(l_p, l_s)
