@@ -113,10 +113,10 @@ constexpr int kWorkQueueStride = 64;
 constexpr int kWorkQueueWords = 16 * kWorkQueueStride;
 
 // The next item of a persistent workgroup on XCD xcd (FwdArgs::persist: a grid of G
-// workgroups took items 0 .. G-1 first).  The remaining items are split by b % 8 == x, the XCD a round-robin
-// dispatch would give them (so xcd_remap's locality holds), over 8 queues of whole query tiles
-// (counter x: items G <= b < n_whole) and 8 queues of tail runs (counter 8 + x: items
-// max(G, n_whole) <= b < n_items), each handed out in increasing order.  The workgroup takes
+// workgroups took items 0 .. G-1 first).  The remaining items are split by b % 8 == x, the XCD
+// a round-robin dispatch would give them (so xcd_remap's locality holds), over 8 queues of whole
+// query tiles (counter x: items G <= b < n_whole) and 8 queues of tail runs (counter 8 + x:
+// items max(G, n_whole) <= b < n_items), each handed out in increasing order.  The workgroup takes
 // from its own XCD's whole-tile queue, then from the others' (the longest items go first), then
 // from the tail queues in the same order; -1 when all are empty.  A queue found empty is marked
 // in `empty` and not asked again.  Relaxed atomics: an item only needs a unique index, and
