@@ -557,10 +557,10 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
             } else {
                 if (ar.persist == 0) break;
                 // thread 0 takes the next item as soon as its wave is done (the atomic's latency
-                // overlaps the drain of the last item's stores) and broadcasts it through one of
-                // two LDS words, alternately: the other waves may still be reading the last
-                // item's word, and every wave read the older one before the last barrier
-                int* const item = (int*)(smem + C::ITEM_ADDR) + (it & 1);
+                // overlaps the drain of the last item's stores) and broadcasts it through an LDS
+                // word: every wave read the word's last value before the barrier that ends the
+                // last segment's prologue, which thread 0 has passed since
+                int* const item = (int*)(smem + C::ITEM_ADDR);
                 if (tid == 0) {
                     const int xcd = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11));  // XCC_ID[3:0]
                     *item = wq_next(ar.wq, xcd, (int)gridDim.x, n_whole, n_whole + ar.sk_wgs, wq_empty);
