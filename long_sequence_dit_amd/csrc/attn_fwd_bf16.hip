@@ -46,8 +46,8 @@
 //    and the transposed reads of V are free of bank conflicts;
 //  * exponentials are base 2 with scale*log2(e) folded into one FMA; the
 //    running output is rescaled only when a row maximum grows by more than
-//    8 (log2 units) past the one it was last rescaled to, and the weights,
-//    taken against that maximum plus 8, stay at most 1.
+//    64 (log2 units) past the one it was last rescaled to, and the weights,
+//    taken against that maximum plus 64, stay at most 1.
 // Workgroups are remapped so that each XCD (workgroups are dealt to the 8
 // XCDs round-robin) runs consecutive query tiles of the same head, which
 // then share K/V tiles in that XCD's L2.
@@ -83,7 +83,14 @@ template <class T>
 using kernarg_t = __attribute__((address_space(4))) const T;
 
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+// Lazy-rescale threshold, log2 units.  bf16 P and the fp32 sums have 8-bit exponents, so a
+// weight taken 64 below the reference is still a normal number with its full mantissa; only
+// weights under 2^-62 times the row max's own could become subnormal (flushed): a relative
+// change far under the fp32 rounding of the sums, even over 10^5 keys.  A large threshold makes
+// the rescale (a VALU pass over the output accumulators, which costs the co-issued MFMA wave
+// cycles) rare: after a row's first tile its reference moves only for a tile whose row max lies
+// more than 64 (log2 units, a factor 2^64 in weight) above the max the reference was set from.
+constexpr float kRescale = 64.0f;
 constexpr int kPrefetch = 4;      // MFMA operands read this many slots ahead
 // The softmax of a tile runs over every slot of the stream (its scores in a second register
 // buffer, so the score MFMAs of the next tile may overwrite the other one meanwhile), rather
@@ -284,6 +291,7 @@ struct Wave {
     f32x16_t acc[D / 32];  // O^T accumulators
     bf16x8_t qf[D / 16];   // Q rows, MFMA B operands
     float m_run;           // softmax reference (scaled, log2 domain): a row max + kRescale
+    float m_max;           // the row's largest raw score so far
     f32x4_t lacc;          // row sums (every element; lanes 16-47 hold their partner's query)
     bf16x8_t rs_a;         // A operand of the row-sum MFMA
     unsigned k_lane[D / 16];  // per-lane LDS read address of K operand kk in K buffer 0
@@ -384,8 +392,11 @@ __device__ __forceinline__ void softmax_slot(Wave<D>& w, Soft& sm, const f32x16_
         // m + kRescale.  So every weight 2^(s c - r) is at most 1 (at most 2^-kRescale right
         // after a move), O and l share the reference (consistent), and LSE = r + log2 l.  A NaN
         // row max (a NaN score) moves the reference to NaN, which makes the rescale factor and
-        // so the row's output and LSE NaN.  Lanes l and l+32 hold the same row and agree.
-        const float m_tile = vmax(sm.m0, sm.m1) * w.c;  // max(m0, m1)
+        // so the row's output and LSE NaN.  Lanes l and l+32 hold the same row and agree.  The
+        // test runs on the running max (at most r before this tile, so it exceeds r exactly
+        // when this tile's max does, and then equals it): one three-input max keeps it.
+        w.m_max = max3(w.m_max, sm.m0, sm.m1);
+        const float m_tile = w.m_max * w.c;
         sm.m_new = !(m_tile <= w.m_run) ? m_tile + kRescale : w.m_run;
         sm.alpha = fast_exp2(w.m_run - sm.m_new);
         w.m_run = sm.m_new;
@@ -644,6 +655,7 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         Wave<D> w;
         w.c = c;
         w.m_run = -INFINITY;
+        w.m_max = -INFINITY;
         w.lacc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         w.rs_a = rowsum_a_operand(lane_it);
         asm volatile("" : "+v"(w.rs_a));  // kept in registers, not rebuilt before every use
@@ -850,7 +862,14 @@ __global__ __launch_bounds__(Cfg<D>::NT, 1) void fwd_bf16_kernel(FwdArgs a, int 
         // slot)
         const float l_tot = from_lane(rowsum_partner(lane_it), w.lacc[0]);
         const float inv_l = 1.f / l_tot;
-        const float lse2 = w.m_run + log2f(l_tot);  // log2 domain
+        // The row sum adds the weights as P.V uses them, rounded to bf16, and O divides by it.
+        // The LSE takes the row's largest weight unrounded: that weight, recomputed exactly as
+        // the key loop computed it (no tile after the max's moved the reference: a move needs a
+        // larger max), replaces its rounded value.  Where one key dominates the row, its
+        // rounding (up to 2^-9 relative) would otherwise be the LSE's error.  A NaN or empty row
+        // gets no correction (the clamped exponential maps NaN to 0).
+        const float e_max = weight_exp2(__builtin_fmaf(w.m_max, w.c, -w.m_run));
+        const float lse2 = w.m_run + log2f(l_tot + (e_max - (float)(__bf16)e_max));  // log2 domain
         if (qrow < ar.Sq) {
             // output element o = wc * acc + wr * O_run (wc = 1/l without a running result)
             float lse_out = lse2 * kLn2, wc = inv_l, wr = 0.f;

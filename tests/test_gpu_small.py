@@ -166,33 +166,92 @@ def test_balanced_tail_spans_query_tiles():
     assert float((l - l_dp).abs().max()) <= 1e-3
 
 
+KERNEL_RESCALE_LOG2 = 64.0  # the bf16 kernel's lazy-rescale threshold (log2 units)
+
+
+def _reference_moves(q, k, D, Skv):
+    """Host-side count, per query row, of the tiles after the first on which the lazy rule moves
+    the row's reference (a tile's scaled row max above the reference, which then goes to that max
+    plus the threshold), from fp64 scores of the bf16 inputs."""
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    kf = synth.bf16_bits_to_f32(k).astype(np.float64)
+    s = np.einsum("bhqd,bhkd->bhqk", qf, kf) * (math.log2(math.e) / math.sqrt(D))
+    ref = np.full(s.shape[:-1], -np.inf)
+    moves = np.zeros(s.shape[:-1], dtype=int)
+    for t in range(0, Skv, 64):
+        m = s[..., t:t + 64].max(-1)
+        mv = m > ref
+        if t > 0:
+            moves += mv
+        ref = np.where(mv, m + KERNEL_RESCALE_LOG2, ref)
+    return moves
+
+
+@pytest.mark.parametrize("growth", [11, 90])
 @pytest.mark.parametrize("D", [128, 64])
-def test_rescale_on_every_tile(D):
-    """Key rows scaled up along the sequence, so that every 64-key tile's row max exceeds the
-    running reference by far more than the lazy-rescale threshold (2^8): the rescale of the
-    output and of the row sums runs on every tile, in every mode."""
+def test_rescale_on_every_tile(D, growth):
+    """Key rows scaled up along the sequence.  growth 11: each 64-key tile's row max grows by
+    about 10 (log2 units), so the weights climb through the lazy-rescale headroom (2^64) and the
+    reference moves 1 to 3 times after the first tile; growth 90: the row max grows by about 80
+    per tile, past the headroom, so the references of the rows of positive sign (about half)
+    move on most tiles and the rescale of the output and row sums runs on nearly every tile, in
+    every mode."""
     B, H, Sq, Skv = 1, 2, 300, 900
     q = synth.normal_rows(31, 0, B, H, Sq, D, kind=synth.KIND_F64)
     k = synth.normal_rows(31, 1, B, H, Skv, D, kind=synth.KIND_F64)
     v = synth.normal_rows(31, 2, B, H, Skv, D)
     # every element of a query row has one sign and every key element is positive, growing along
-    # the keys: for the rows of positive sign the tile max grows by about 12 (log2 units) per
-    # tile, so those rows move their reference on 8 to 13 of the 13 tiles after the first (each
-    # wave rescales on every tile); rows of negative sign keep their first tile's max
+    # the keys; rows of negative sign keep their first tile's reference
     q = synth.f32_to_bf16_bits((np.sign(q.sum(-1, keepdims=True)) * np.abs(q)).astype(np.float32))
-    k = synth.f32_to_bf16_bits((np.abs(k) * (0.05 + 11 * np.arange(Skv) / 64.0)[None, None, :, None] /
+    k = synth.f32_to_bf16_bits((np.abs(k) * (0.05 + growth * np.arange(Skv) / 64.0)[None, None, :, None] /
                                 math.sqrt(D)).astype(np.float32))
+    moves = _reference_moves(q, k, D, Skv)
+    if growth == 11:
+        assert 1 <= moves.max() <= 3
+    else:  # 13 tiles after the first: rows of positive sign (about half) move on 8 or more
+        assert moves.max() == 13 and np.count_nonzero(moves >= 8) >= 0.4 * moves.size
     scale = 1 / math.sqrt(D)
     o_ref, l_ref = oracle.attention(q, k, v, scale)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     o, l = A().chunk_fwd(qd, kd, vd, scale)
     torch.cuda.synchronize()
-    assert_parity(o, l, o_ref, l_ref, what="rescale every tile D=%d" % D)
+    assert_parity(o, l, o_ref, l_ref, what="rescale growth %d D=%d" % (growth, D))
     for mode in ("fused", "nway", "online"):
         ws = torch.empty(max(A().shard_workspace_size(B, H, Sq, D, 3, mode), 1), dtype=torch.uint8, device="cuda")
         o, l = A().shard_fwd(qd, kd, vd, (300, 350, 250), (2, 0, 1), mode=mode, workspace=ws)
         torch.cuda.synchronize()
-        assert_parity(o, l, o_ref, l_ref, what="rescale every tile D=%d %s" % (D, mode))
+        assert_parity(o, l, o_ref, l_ref, what="rescale growth %d D=%d %s" % (growth, D, mode))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_lse_of_rows_dominated_by_one_key(D):
+    """Each query row i has one planted key (key i, along q_i, with a score of 20 natural units;
+    no other score of the row above 9 for D = 128, 14 for D = 64), which carries nearly all of
+    the row's weight.  P.V and the
+    row sum use the weights rounded to bf16, so the LSE would carry that key's rounding (up to
+    2^-9 relative, about 1e-3 on average); the kernel's LSE takes the row's largest weight
+    unrounded, so its error stays at fp32 level: 1e-4 on every row, in every mode (the key in
+    one chunk of three, a balanced tail where there is one), while O stays within the bf16 gate."""
+    B, H, Sq, Skv = 1, 2, 600, 900
+    q64 = synth.normal_rows(61, 0, B, H, Sq, D, kind=synth.KIND_F64)
+    k64 = synth.normal_rows(61, 1, B, H, Skv, D, kind=synth.KIND_F64)
+    v = synth.normal_rows(61, 2, B, H, Skv, D)
+    qn = q64 / np.linalg.norm(q64, axis=-1, keepdims=True)
+    k64[:, :, :Sq] = 20.0 * math.sqrt(D) * qn / np.linalg.norm(q64, axis=-1, keepdims=True)
+    q = synth.f32_to_bf16_bits(q64.astype(np.float32))
+    k = synth.f32_to_bf16_bits(k64.astype(np.float32))
+    scale = 1 / math.sqrt(D)
+    o_ref, l_ref = oracle.attention(q, k, v, scale)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    runs = [("chunk", A().chunk_fwd(qd, kd, vd, scale))]
+    for mode in ("fused", "nway", "online"):
+        runs.append((mode, A().shard_fwd(qd, kd, vd, (300, 350, 250), (2, 0, 1), mode=mode)))
+    torch.cuda.synchronize()
+    for what, (o, l) in runs:
+        err = float(np.abs(to_f64(l) - l_ref).max())
+        print("dominant key, D=%d %s: LSE max-abs %.3g" % (D, what, err), flush=True)
+        assert err <= 1e-4, (what, err)
+        assert_parity(o, l, o_ref, l_ref, what="dominant key D=%d %s" % (D, what))
 
 
 def test_bf16_chunk_partials_and_merge():
